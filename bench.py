@@ -1,0 +1,165 @@
+#!/usr/bin/env python3
+"""Benchmark of the Ozaki II FP64 GEMM emulation on one MI355X.
+
+A step is one whole ozaki2_dgemm call (scaling, residues, s INT8 GEMMs, CRT) on the
+synthetic workload, inputs already resident in HBM.  The metric is effective FP64
+TFLOPS = 2 p q r / t ("Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part I
+section 3).  Stage times come from HIP events the library records on the launch
+stream between its stages; the GEMM stage is one kernel launch (all s moduli), so its
+average event interval is that kernel's average launch duration.
+
+Prints one JSON line.  Only one GPU is supported: --gpus above 1 exits with a message.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks used for the rooflines
+PEAK_INT8_TOPS = 5000.0     # dense INT8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0       # HBM3E, GB/s
+# Pages' number for this metric and workload (GH200, fast-14, n = 8192; paper Table 3)
+PAGES_FAST14_N8192_GH200 = 72.1
+
+
+def stage_bytes(n_p, n_q, n_r, s, accu):
+    """Algorithmic HBM bytes per call of each memory-bound stage."""
+    a_elems, b_elems = n_p * n_q, n_q * n_r
+    scaling = 8 * (a_elems + b_elems) * (2 if accu else 1) + (2 * (a_elems + b_elems) if accu else 0)
+    residues = 8 * (a_elems + b_elems) + s * (a_elems + b_elems)
+    crt = s * n_p * n_r + 8 * n_p * n_r
+    return scaling, residues, crt
+
+
+def cpu_baseline(A, B, s, mode, rows, cols):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    t0 = time.perf_counter()
+    oracle.ozaki2_sample(A, B, s, mode, np.arange(rows), np.arange(cols))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * A.shape[1] * cols
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "effective FP64 TFLOPS",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"C[0:{rows}, 0:{cols}] of the {A.shape[0]}x{A.shape[1]}x{B.shape[1]} workload "
+                  f"(scalings of the sampled rows/columns, their residues, s products, CRT, inverse scaling)",
+        "seconds": dt,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="n8192_fast_s14")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=32)
+    ap.add_argument("--cpu-cols", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the emulated GEMM is "
+              f"measured on one MI355X only", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fp64_gemm_emulation_amd import binding
+    from fp64_gemm_emulation_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    n, s, accu = w.n, w.s, w.mode == "accu"
+    A, B = w.inputs()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Ad = binding.colmajor(torch.from_numpy(np.ascontiguousarray(A)).to(dev))
+    Bd = binding.colmajor(torch.from_numpy(np.ascontiguousarray(B)).to(dev))
+    C = binding.empty_colmajor(n, n, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
+    torch.cuda.synchronize()
+
+    assert binding.ozaki2_timing_begin(args.steps) == binding.OZ2_OK
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc, stage_ms, ncalls = binding.ozaki2_timing_end()
+    assert rc == binding.OZ2_OK and ncalls == args.steps
+    rc, flags = binding.ozaki2_get_flags()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    eff_tflops = 2.0 * n ** 3 / (ms_per_step * 1e-3) / 1e12
+    st = [v / ncalls for v in stage_ms]
+    gemm_ops = s * 2.0 * n ** 3
+    gemm_tops = gemm_ops / (st[2] * 1e-3) / 1e12
+    sb, rb, cb = stage_bytes(n, n, n, s, accu)
+    total_stage = sum(st)
+    stages = {
+        "scaling_ms": st[0], "residues_ms": st[1], "gemm_ms": st[2], "crt_ms": st[3],
+        "preprocess_fraction": (st[0] + st[1]) / total_stage,
+        "residues_GBs": rb / (st[1] * 1e-3) / 1e9,
+        "residues_frac_hbm": rb / (st[1] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "scaling_GBs": sb / (st[0] * 1e-3) / 1e9,
+        "crt_GBs": cb / (st[3] * 1e-3) / 1e9,
+        "crt_frac_hbm": cb / (st[3] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "gemm_frac_int8_peak": gemm_tops / PEAK_INT8_TOPS,
+        "residues_per_s": 2.0 * s * n * n / (st[1] * 1e-3),
+        "int8_macs_per_s": s * float(n) ** 3 / (st[2] * 1e-3),
+    }
+    result = {
+        "metric": "effective FP64 TFLOPS (2n^3/t), n=8192 fast-14; per-stage ms breakdown",
+        "value": eff_tflops,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (eff_tflops / PAGES_FAST14_N8192_GH200) if args.workload == "n8192_fast_s14" else None,
+        "baseline_ref": "pages: GH200 fast-14 n=8192, 72.1 effective TFLOPS (paper Table 3), other hardware",
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": n, "mode": w.mode, "s": s, "phi": w.phi,
+                   "seeds": [w.seed_a, w.seed_b], "inputs": "f64 column-major, resident in HBM"},
+        "stages": stages,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_i8_kernel (s batched INT8 GEMMs + mod epilogue)",
+            "achieved": gemm_tops,
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tops / PEAK_INT8_TOPS,
+            "traffic": None,
+        },
+        "nonfinite_flag": bool(flags & 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(A, B, s, w.mode, args.cpu_rows, args.cpu_cols)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+// oz2_crt.hip -- reconstruction: X = CRT_M(R_1..R_s) in [-M/2, M/2) and C = D^-1 X E^-1
+// ("Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part I section 1, red stage).
+//
+// X is computed exactly: with W_t = (M/m_t) ((M/m_t)^-1 mod m_t),
+//   X = sum_t R_t W_t - k M,   k = round(sum_t R_t W_t / M) = round(sum_t R_t c_t),
+//   c_t = ((M/m_t)^-1 mod m_t) / m_t.
+// W_t and M are split into 32-bit limbs held in doubles, so every limb sum is an exact
+// FP64 integer FMA chain (each partial sum < 20 * 2^8 * 2^32 < 2^53).  k is exact: the
+// scalings keep |X| <= 2^tau, so sum_t R_t c_t lies at least 0.014 (over all s = 2..20)
+// away from a half-integer, far above its FP64 rounding error (< 2^-35).  The limbs are
+// carried into a two's-complement multiword integer and converted to FP64 with one
+// round-to-nearest-even, then scaled by 2^-(d_i + b_j) with ldexp (exact unless the
+// result is subnormal).
+#include "oz2_common.hpp"
+#include "oz2_internal.hpp"
+
+namespace oz2 {
+
+// Round the magnitude held in words w[0..L-1] (little-endian) to a double with exponent
+// offset `scale`: returns RN(w) * 2^scale.
+template <int L>
+__device__ __forceinline__ double words_to_double(const uint32_t (&w)[L], int scale) {
+  int h = 0;
+#pragma unroll
+  for (int k = 1; k < L; ++k)
+    if (w[k] != 0) h = k;
+  uint32_t w2 = 0, w1 = 0, w0 = 0;
+  bool sticky = false;
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    if (k == h) w2 = w[k];
+    if (k == h - 1) w1 = w[k];
+    if (k == h - 2) w0 = w[k];
+    if (k < h - 2) sticky |= w[k] != 0;
+  }
+  if (w2 == 0) return 0.0;  // then h == 0 and the value is 0
+  const int lz = __clz(static_cast<int>(w2));
+  uint64_t top = (static_cast<uint64_t>(w2) << 32) | w1;
+  if (lz > 0) {
+    top = (top << lz) | (static_cast<uint64_t>(w0) >> (32 - lz));
+    sticky |= (w0 << lz) != 0;
+  } else {
+    sticky |= w0 != 0;
+  }
+  // bit 63 of top is the leading one; keep 53 bits and round to nearest even
+  uint64_t mant = top >> 11;
+  const bool rbit = ((top >> 10) & 1ull) != 0;
+  sticky |= (top & 0x3FFull) != 0;
+  if (rbit && (sticky || (mant & 1ull))) mant += 1;  // may reach 2^53: still exact
+  const int e2 = 32 * h + 31 - lz - 52;
+  return ldexp(static_cast<double>(mant), e2 + scale);
+}
+
+template <int S, bool DUMPX>
+__global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ res, long r_plane, int ldr, int p,
+                                                  int r, int pq4, const int* __restrict__ d,
+                                                  const int* __restrict__ b, double* __restrict__ C, long ldc,
+                                                  uint32_t* __restrict__ x_dump) {
+  constexpr int L = CrtTable<S>::L;
+  // grid: x = column j, y = groups of 256 quads of rows
+  const int j = blockIdx.x;
+  const int iq = blockIdx.y * blockDim.x + threadIdx.x;
+  if (iq >= pq4) return;
+  const int i4 = iq * 4;
+  uint32_t rw[S];
+  const uint8_t* src = res + static_cast<long>(j) * ldr + i4;
+#pragma unroll
+  for (int t = 0; t < S; ++t) rw[t] = *reinterpret_cast<const uint32_t*>(src + t * r_plane);
+  const int bj = b[j];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int i = i4 + v;
+    if (i >= p) break;
+    double acc[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) acc[k] = 0.0;
+    double f = 0.0;
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      const double rt = static_cast<double>((rw[t] >> (8 * v)) & 0xFFu);
+      f = fma(rt, kCrt<S>.c[t], f);
+#pragma unroll
+      for (int k = 0; k < L; ++k) acc[k] = fma(rt, kCrt<S>.w[t][k], acc[k]);
+    }
+    const double kq = rint(f);
+#pragma unroll
+    for (int k = 0; k < L; ++k) acc[k] = fma(-kq, kCrt<S>.m[k], acc[k]);
+    // carry into 32-bit words (two's complement, top word signed)
+    uint32_t wd[L];
+#pragma unroll
+    for (int k = 0; k < L - 1; ++k) {
+      const double cy = floor(acc[k] * 0x1p-32);
+      wd[k] = static_cast<uint32_t>(fma(-cy, 0x1p32, acc[k]));
+      acc[k + 1] += cy;
+    }
+    const int top = static_cast<int>(acc[L - 1]);
+    wd[L - 1] = static_cast<uint32_t>(top);
+    if constexpr (DUMPX) {
+      uint32_t* xd = x_dump + (static_cast<long>(j) * p + i) * 5;
+#pragma unroll
+      for (int k = 0; k < 5; ++k) xd[k] = k < L ? wd[k] : (top < 0 ? 0xFFFFFFFFu : 0u);
+    }
+    const bool neg = top < 0;
+    if (neg) {  // magnitude = ~X + 1
+      uint32_t carry = 1;
+#pragma unroll
+      for (int k = 0; k < L; ++k) {
+        const uint32_t nv = ~wd[k] + carry;
+        carry = (carry != 0 && nv == 0) ? 1u : 0u;
+        wd[k] = nv;
+      }
+    }
+    const double mag = words_to_double<L>(wd, -(d[i] + bj));
+    C[i + static_cast<long>(j) * ldc] = neg ? -mag : mag;
+  }
+}
+
+template <int S>
+static void launch_crt_s(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st) {
+  const int pq4 = (w.p + 3) / 4;
+  if (pq4 == 0 || w.r == 0) return;
+  const dim3 blocks(w.r, (pq4 + 255) / 256);
+  const long r_plane = static_cast<long>(w.r_pad) * w.p_pad;
+  if (dump.x != nullptr)
+    hipLaunchKernelGGL((crt_kernel<S, true>), blocks, dim3(256), 0, st, w.res, r_plane, w.p_pad, w.p, w.r,
+                       pq4, w.d, w.b, C, ldc, dump.x);
+  else
+    hipLaunchKernelGGL((crt_kernel<S, false>), blocks, dim3(256), 0, st, w.res, r_plane, w.p_pad, w.p, w.r,
+                       pq4, w.d, w.b, C, ldc, nullptr);
+}
+
+template <int S>
+static bool dispatch_crt(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st) {
+  if constexpr (S > kMaxS) {
+    return false;
+  } else {
+    if (w.s == S) {
+      launch_crt_s<S>(w, C, ldc, dump, st);
+      return true;
+    }
+    return dispatch_crt<S + 1>(w, C, ldc, dump, st);
+  }
+}
+
+hipError_t launch_crt(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st) {
+  if (!dispatch_crt<kMinS>(w, C, ldc, dump, st)) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace oz2

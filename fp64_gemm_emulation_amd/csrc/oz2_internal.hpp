@@ -1,0 +1,68 @@
+// oz2_internal.hpp -- host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace oz2 {
+
+// Device pointers into one call's workspace (see the layout in oz2_api.hip).
+struct Work {
+  int p, q, r, s;
+  bool accu;
+  int p_pad, r_pad, q_pad;  // rows of A_t / B_t padded to kRowPad, inner dim to kKPad
+  int nch;                  // number of kChunk-long blocks along q
+  int tau;
+  unsigned* flags;          // 1 word
+  int* d;                   // [p]   row exponents of A
+  int* b;                   // [r]   column exponents of B
+  int* part_e_a;            // [p * nch]
+  double* part_s_a;         // [p * nch]
+  int* part_e_b;            // [r * nch]
+  double* part_s_b;         // [r * nch]
+  int* e_row;               // [p]   accu: max-abs exponents of rows of A
+  int* f_col;               // [r]   accu: max-abs exponents of columns of B
+  int* rho;                 // [p]   accu: row maxima of the bound product
+  int* gamma;               // [r]   accu: column maxima of the bound product
+  int8_t* at;               // [s][p_pad][q_pad]  A_t (K-permuted in 256-blocks)
+  int8_t* bt;               // [s][r_pad][q_pad]  B_t (same K permutation)
+  int8_t* abar;             // [p_pad][q_pad]     accu bound inputs (alias of A_t plane 0)
+  int8_t* bbar;             // [r_pad][q_pad]     (alias of B_t plane 0)
+  uint8_t* res;             // [s][r_pad][p_pad]  R_t, column-major planes
+};
+
+// Optional validation outputs written while the pipeline runs.
+struct DumpPtrs {
+  double* ap = nullptr;     // A' column-major, ld p
+  double* bp = nullptr;     // B' column-major, ld q
+  int32_t* pt = nullptr;    // P_t [s][r][p]
+  uint32_t* x = nullptr;    // X   [r][p][5]
+};
+
+// scaling stage
+hipError_t launch_fill_i32(int* ptr, int value, long n, hipStream_t st);
+hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st);
+hipError_t launch_fast_scaling(const double* A, long lda, const double* B, long ldb, const Work& w,
+                               hipStream_t st);
+hipError_t launch_accu_bound_inputs(const double* A, long lda, const double* B, long ldb, const Work& w,
+                                    hipStream_t st);
+hipError_t launch_accu_exponents(const Work& w, hipStream_t st);
+
+// residue stage
+hipError_t launch_residues(const double* A, long lda, const double* B, long ldb, const Work& w,
+                           const DumpPtrs& dump, hipStream_t st);
+
+// GEMM stage: epi 0 = R_t only, 1 = R_t and raw P_t dump, 2 = accu bound (rho, gamma)
+hipError_t launch_gemm(const Work& w, int epi, const DumpPtrs& dump, hipStream_t st);
+
+// reconstruction stage
+hipError_t launch_crt(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st);
+
+// validation helpers: undo the K permutation / padding of an int8 operand plane set
+// src [planes][rows_pad][q_pad] -> dst [planes][rows][q]
+hipError_t launch_unpermute_i8(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
+                               int8_t* dst, hipStream_t st);
+
+}  // namespace oz2

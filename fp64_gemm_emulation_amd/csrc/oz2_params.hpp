@@ -1,0 +1,221 @@
+// oz2_params.hpp -- compile-time constants of the Ozaki II emulation.
+//
+// Everything here is derived at compile time from two definitions:
+//   * the moduli: pairwise coprime, at most 256 so centered residues fit int8
+//     ("Ozaki II supplement: INT8 range conditions and paper performance results",
+//     section 1.2), taken greedily downward from 256;
+//   * M = prod m_t and the reconstruction range [-M/2, M/2) of the CRT
+//     ("Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part I section 1).
+// The scalings keep |(A'B')_ij| <= 2^tau with tau = floor(log2(M/2 - 1)).
+#pragma once
+
+#include <cstdint>
+
+namespace oz2 {
+
+constexpr int kMinS = 2;
+constexpr int kMaxS = 20;
+
+// Fast-mode bound: |a| quantized upward to kFBits fractional bits relative to the
+// max-abs exponent of its kChunk-long block; accu-mode bound inputs are integers
+// in [0, 2^kQBits].
+constexpr int kFBits = 20;
+constexpr int kChunk = 256;
+constexpr int kQBits = 6;
+constexpr int kNoExp = -(1 << 30);  // exponent of an all-zero line / block
+
+// ---------------------------------------------------------------------------
+// Moduli
+// ---------------------------------------------------------------------------
+constexpr int gcd_c(int a, int b) {
+  while (b != 0) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+struct ModTable {
+  int m[kMaxS];
+};
+
+constexpr ModTable make_moduli() {
+  ModTable tab{};
+  int n = 0;
+  for (int c = 256; n < kMaxS && c >= 2; --c) {
+    bool ok = true;
+    for (int k = 0; k < n; ++k)
+      if (gcd_c(c, tab.m[k]) != 1) ok = false;
+    if (ok) tab.m[n++] = c;
+  }
+  return tab;
+}
+
+inline constexpr ModTable kModTable = make_moduli();
+constexpr int modulus(int t) { return kModTable.m[t]; }
+
+static_assert(modulus(0) == 256 && modulus(1) == 255 && modulus(7) == 233 && modulus(13) == 199,
+              "greedy pairwise-coprime moduli from 256");
+
+// ---------------------------------------------------------------------------
+// Small fixed-width unsigned big integers (little-endian 32-bit limbs)
+// ---------------------------------------------------------------------------
+constexpr int kBigLimbs = 6;  // 192 bits > log2(M) for s <= 20 (about 155.4)
+
+struct Big {
+  uint32_t w[kBigLimbs];
+};
+
+constexpr Big big_one() {
+  Big b{};
+  b.w[0] = 1;
+  return b;
+}
+
+constexpr Big big_mul_small(Big a, uint32_t m) {
+  uint64_t carry = 0;
+  for (int k = 0; k < kBigLimbs; ++k) {
+    uint64_t v = static_cast<uint64_t>(a.w[k]) * m + carry;
+    a.w[k] = static_cast<uint32_t>(v);
+    carry = v >> 32;
+  }
+  return a;
+}
+
+constexpr Big big_shr1(Big a) {
+  for (int k = 0; k < kBigLimbs; ++k) {
+    uint32_t hi = (k + 1 < kBigLimbs) ? a.w[k + 1] : 0u;
+    a.w[k] = (a.w[k] >> 1) | (hi << 31);
+  }
+  return a;
+}
+
+constexpr Big big_dec(Big a) {  // a - 1, a >= 1
+  for (int k = 0; k < kBigLimbs; ++k) {
+    if (a.w[k] != 0) {
+      a.w[k] -= 1;
+      break;
+    }
+    a.w[k] = 0xFFFFFFFFu;
+  }
+  return a;
+}
+
+constexpr int big_bitlen(Big a) {
+  for (int k = kBigLimbs - 1; k >= 0; --k) {
+    if (a.w[k] != 0) {
+      int b = 0;
+      uint32_t v = a.w[k];
+      while (v) {
+        ++b;
+        v >>= 1;
+      }
+      return 32 * k + b;
+    }
+  }
+  return 0;
+}
+
+constexpr uint32_t big_mod_small(Big a, uint32_t m) {
+  uint64_t r = 0;
+  for (int k = kBigLimbs - 1; k >= 0; --k) r = ((r << 32) | a.w[k]) % m;
+  return static_cast<uint32_t>(r);
+}
+
+// prod_{t < S, t != skip} m_t
+constexpr Big product_except(int S, int skip) {
+  Big b = big_one();
+  for (int t = 0; t < S; ++t)
+    if (t != skip) b = big_mul_small(b, static_cast<uint32_t>(modulus(t)));
+  return b;
+}
+
+constexpr Big modulus_product(int S) { return product_except(S, -1); }
+
+// tau = floor(log2(M/2 - 1))
+constexpr int tau_of(int S) { return big_bitlen(big_dec(big_shr1(modulus_product(S)))) - 1; }
+
+constexpr uint32_t inv_mod(uint32_t a, uint32_t m) {
+  a %= m;
+  for (uint32_t x = 1; x < m; ++x)
+    if ((a * x) % m == 1) return x;
+  return 0;
+}
+
+constexpr uint32_t pow2_mod(int e, uint32_t m) {
+  uint32_t r = 1 % m;
+  for (int k = 0; k < e; ++k) r = (r * 2) % m;
+  return r;
+}
+
+static_assert(tau_of(2) == 14 && tau_of(8) == 62 && tau_of(14) == 109 && tau_of(18) == 139,
+              "tau = floor(log2(M/2 - 1))");
+
+// ---------------------------------------------------------------------------
+// Residue kernel: limb layout of |A'| and per-modulus constants
+// ---------------------------------------------------------------------------
+// |A'| is split into a low limb of kLimb0 bits and NLHI limbs of kLimbHi bits.  For
+// an odd modulus m the reduced value z = L0 + sum_k c_k L_k (c_k the centered residue
+// of 2^(bit offset of limb k)) satisfies |z| < 2^22 + NLHI * 127 * 2^12 < 2^23, so
+// it is exact in FP32 and its nearest quotient by m can be taken in FP32.
+constexpr int kLimb0 = 22;
+constexpr int kLimbHi = 12;
+
+// Bit length bound of |A'|: fast keeps ||2^d_i A(i,:)||_2 <= 2^(tau/2); accu keeps
+// |A'| < 2^(floor(tau/2) + kQBits).
+constexpr int max_bits(int S, bool accu) { return accu ? tau_of(S) / 2 + kQBits : tau_of(S) / 2 + 1; }
+
+constexpr int nl_hi(int S, bool accu) {
+  int extra = max_bits(S, accu) - kLimb0;
+  return extra <= 0 ? 0 : (extra + kLimbHi - 1) / kLimbHi;
+}
+
+static_assert(nl_hi(kMaxS, true) <= 8, "|z| < 2^23 needs at most 8 high limbs");
+
+constexpr int centered_small(uint32_t r, uint32_t m) {
+  return (r > (m - 1) / 2) ? static_cast<int>(r) - static_cast<int>(m) : static_cast<int>(r);
+}
+
+// coefficient of high limb k (1-based) for modulus t: rho_m(2^(kLimb0 + kLimbHi (k-1)))
+constexpr int limb_coef(int t, int k) {
+  return centered_small(pow2_mod(kLimb0 + kLimbHi * (k - 1), static_cast<uint32_t>(modulus(t))),
+                        static_cast<uint32_t>(modulus(t)));
+}
+
+// ---------------------------------------------------------------------------
+// CRT constants: X = sum_t R_t W_t - k M, W_t = (M / m_t) * ((M / m_t)^-1 mod m_t),
+// k = rint(sum_t R_t c_t), c_t = W_t / M = ((M / m_t)^-1 mod m_t) / m_t.
+// W_t and M are held as 32-bit limbs stored in doubles so the weighted sums are exact
+// FP64 integer FMAs (every partial sum stays below 20 * 2^8 * 2^32 < 2^53).
+// ---------------------------------------------------------------------------
+constexpr int crt_limbs(int S) { return (big_bitlen(modulus_product(S)) + 31) / 32; }
+
+template <int S>
+struct CrtTable {
+  static constexpr int L = crt_limbs(S);
+  double w[S][L];
+  double c[S];
+  double m[L];
+};
+
+template <int S>
+constexpr CrtTable<S> make_crt() {
+  CrtTable<S> tab{};
+  Big M = modulus_product(S);
+  for (int k = 0; k < CrtTable<S>::L; ++k) tab.m[k] = static_cast<double>(M.w[k]);
+  for (int t = 0; t < S; ++t) {
+    uint32_t mt = static_cast<uint32_t>(modulus(t));
+    Big rest = product_except(S, t);
+    uint32_t inv = inv_mod(big_mod_small(rest, mt), mt);
+    Big w = big_mul_small(rest, inv);
+    for (int k = 0; k < CrtTable<S>::L; ++k) tab.w[t][k] = static_cast<double>(w.w[k]);
+    tab.c[t] = static_cast<double>(inv) / static_cast<double>(mt);
+  }
+  return tab;
+}
+
+template <int S>
+inline constexpr CrtTable<S> kCrt = make_crt<S>();
+
+}  // namespace oz2

@@ -1,0 +1,323 @@
+// oz2_scaling.hip -- scaling stage: the power-of-two exponents d (rows of A) and b
+// (columns of B) that define D = diag(2^d) and E = diag(2^b).
+//
+// fast ("Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part I section 2 and
+// Part II section 5.1): Cauchy-Schwarz bound from per-line max-abs and sum of squares,
+// sums rounded upward so the bound is never underestimated.  Here the sum of squares
+// is taken exactly on integers: in every kChunk-long block with max-abs exponent e_c,
+// u = ceil(|a| 2^(kFBits - e_c)) and S_c = sum u^2; blocks combine as
+// S = sum_c ceil(S_c / 4^(e - e_c)) with e the line's max-abs exponent.  Then
+// d = floor((tau - ceil(log2 S)) / 2) + kFBits - e, the largest exponent that keeps the
+// scaled squared-norm bound within the budget 2^tau split equally between the row of A
+// and the column of B.
+//
+// accu (same page, section 2 and 5.1 "accu"): |A| and |B| quantized upward into
+// integers in [0, 2^kQBits] relative to each line's max-abs exponent, one INT8 bound
+// GEMM (oz2_gemm.hip), row / column maxima rho, gamma of its output, then
+// d = floor((tau - ceil(log2 max(rho, 1))) / 2) + kQBits - e.
+#include "oz2_common.hpp"
+#include "oz2_internal.hpp"
+
+namespace oz2 {
+
+__global__ void fill_i32_kernel(int* __restrict__ p, int v, long n) {
+  long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void fill_u32_kernel(unsigned* __restrict__ p, unsigned v, long n) {
+  long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Rows of column-major A: 64 rows (one per lane) x one kChunk block per workgroup;
+// wave w reads l in [c kChunk + 64 w, +64).  Each load instruction reads 64 consecutive
+// rows of one column.  MAXONLY: only the block max-abs exponents are produced.
+template <bool MAXONLY>
+__global__ __launch_bounds__(256) void stats_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
+                                                         int nch, int* __restrict__ part_e,
+                                                         double* __restrict__ part_s,
+                                                         unsigned* __restrict__ flags) {
+  __shared__ int sh_e[4][kWave];
+  __shared__ double sh_s[4][kWave];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int i = blockIdx.x * kWave + lane;
+  const int c = blockIdx.y;
+  const int l0 = c * kChunk + w * kWave;
+  const bool row_ok = i < p;
+  const double* base = A + (row_ok ? i : 0) + static_cast<long>(l0) * lda;
+
+  double v[kWave];
+  int emax = kNoExp;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < kWave; ++k) {
+    double x = 0.0;
+    if (row_ok && l0 + k < q) x = base[static_cast<long>(k) * lda];
+    const bool nf = is_nonfinite(x);
+    bad |= nf;
+    x = nf ? 0.0 : x;
+    v[k] = x;
+    emax = max(emax, exponent_of(x));
+  }
+  if (bad) atomicOr(flags, kFlagNonFinite);
+  sh_e[w][lane] = emax;
+  __syncthreads();
+  const int ec = max(max(sh_e[0][lane], sh_e[1][lane]), max(sh_e[2][lane], sh_e[3][lane]));
+  if constexpr (MAXONLY) {
+    if (w == 0 && row_ok) part_e[static_cast<long>(i) * nch + c] = ec;
+    return;
+  } else {
+    double acc = 0.0;  // exact: at most 64 * 2^40
+    if (ec != kNoExp) {
+#pragma unroll
+      for (int k = 0; k < kWave; ++k) {
+        const double u = ceil_scaled_abs(v[k], exponent_of(v[k]), kFBits - ec);
+        acc = fma(u, u, acc);
+      }
+    }
+    sh_s[w][lane] = acc;
+    __syncthreads();
+    if (w == 0 && row_ok) {
+      part_e[static_cast<long>(i) * nch + c] = ec;
+      part_s[static_cast<long>(i) * nch + c] = (sh_s[0][lane] + sh_s[1][lane]) + (sh_s[2][lane] + sh_s[3][lane]);
+    }
+  }
+}
+
+// Columns of column-major B (contiguous): one wave per (column j, block c); lane reads
+// l = c kChunk + lane + 64 k, k = 0..3, so every load instruction is 512 contiguous bytes.
+template <bool MAXONLY>
+__global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
+                                                         int nch, int* __restrict__ part_e,
+                                                         double* __restrict__ part_s,
+                                                         unsigned* __restrict__ flags) {
+  // grid: x = column j, y = groups of 4 blocks; one wave per (j, c)
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x;
+  const int c = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (c >= nch) return;  // whole wave
+  const double* col = B + static_cast<long>(j) * ldb;
+  double v[4];
+  int emax = kNoExp;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int l = c * kChunk + lane + kWave * k;
+    double x = l < q ? col[l] : 0.0;
+    const bool nf = is_nonfinite(x);
+    bad |= nf;
+    x = nf ? 0.0 : x;
+    v[k] = x;
+    emax = max(emax, exponent_of(x));
+  }
+  if (bad) atomicOr(flags, kFlagNonFinite);
+  const int ec = wave_max(emax);
+  const long slot = static_cast<long>(j) * nch + c;
+  if constexpr (MAXONLY) {
+    if (lane == 0) part_e[slot] = ec;
+  } else {
+    double acc = 0.0;
+    if (ec != kNoExp) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double u = ceil_scaled_abs(v[k], exponent_of(v[k]), kFBits - ec);
+        acc = fma(u, u, acc);
+      }
+    }
+    acc = wave_sum(acc);  // exact: at most 256 * 2^40
+    if (lane == 0) {
+      part_e[slot] = ec;
+      part_s[slot] = acc;
+    }
+  }
+}
+
+// One thread per line (rows of A first, then columns of B): combine block partials.
+__global__ void fast_exponents_kernel(int na, int nb, int nch, const int* __restrict__ pe_a,
+                                      const double* __restrict__ ps_a, const int* __restrict__ pe_b,
+                                      const double* __restrict__ ps_b, int* __restrict__ d,
+                                      int* __restrict__ b, int tau) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= na + nb) return;
+  const bool is_a = idx < na;
+  const int line = is_a ? idx : idx - na;
+  const int* pe = (is_a ? pe_a : pe_b) + static_cast<long>(line) * nch;
+  const double* ps = (is_a ? ps_a : ps_b) + static_cast<long>(line) * nch;
+  int e = kNoExp;
+  for (int c = 0; c < nch; ++c) e = max(e, pe[c]);
+  int out = 0;
+  if (e != kNoExp) {
+    uint64_t S = 0;
+    for (int c = 0; c < nch; ++c) S += ceil_shift(ps[c], 2 * (e - pe[c]));
+    out = ((tau - clog2_u64(S)) >> 1) + kFBits - e;
+  }
+  if (is_a)
+    d[line] = out;
+  else
+    b[line] = out;
+}
+
+// accu: line max-abs exponents from block maxima.
+__global__ void max_exponents_kernel(int na, int nb, int nch, const int* __restrict__ pe_a,
+                                     const int* __restrict__ pe_b, int* __restrict__ e_row,
+                                     int* __restrict__ f_col) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= na + nb) return;
+  const bool is_a = idx < na;
+  const int line = is_a ? idx : idx - na;
+  const int* pe = (is_a ? pe_a : pe_b) + static_cast<long>(line) * nch;
+  int e = kNoExp;
+  for (int c = 0; c < nch; ++c) e = max(e, pe[c]);
+  if (is_a)
+    e_row[line] = e;
+  else
+    f_col[line] = e;
+}
+
+// accu bound inputs of the rows of A: Abar_il = ceil(|a_il| 2^(kQBits - e_i)) in [0, 64],
+// written in the K-permuted operand layout [p_pad][q_pad] (zeros in the padding).
+// Workgroup: 64 rows (lane) x 4 lanes-of-16 L; thread covers l = 256 blk + L + 16 k.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
+                                                         int q_pad, const int* __restrict__ e_row,
+                                                         int8_t* __restrict__ abar) {
+  const int lane = threadIdx.x & 63;
+  const int L = (blockIdx.y & 3) * 4 + (threadIdx.x >> 6);
+  const int blk = blockIdx.y >> 2;
+  const int i = blockIdx.x * kWave + lane;
+  const bool row_ok = i < p;
+  const int e = row_ok ? e_row[i] : kNoExp;
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  if (e != kNoExp) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int l = blk * kKPad + L + 16 * k;
+      double x = l < q ? A[i + static_cast<long>(l) * lda] : 0.0;
+      x = is_nonfinite(x) ? 0.0 : x;
+      const uint32_t qv = static_cast<uint32_t>(ceil_scaled_abs(x, exponent_of(x), kQBits - e));
+      packed[k >> 2] |= qv << (8 * (k & 3));
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(abar + static_cast<long>(i) * q_pad + blk * kKPad + 16 * L);
+  *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
+// accu bound inputs of the columns of B (contiguous): groups of 16 lanes per 256-block.
+__global__ __launch_bounds__(256) void quant_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
+                                                         int q_pad, int nblk, const int* __restrict__ f_col,
+                                                         int8_t* __restrict__ bbar) {
+  // grid: x = column j, y = groups of 16 consecutive 256-blocks
+  const int L = threadIdx.x & 15;
+  const int blk = blockIdx.y * 16 + (threadIdx.x >> 4);
+  if (blk >= nblk) return;
+  const int j = blockIdx.x;
+  const bool col_ok = j < r;
+  const int f = col_ok ? f_col[j] : kNoExp;
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  if (f != kNoExp) {
+    const double* col = B + static_cast<long>(j) * ldb;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int l = blk * kKPad + L + 16 * k;
+      double x = l < q ? col[l] : 0.0;
+      x = is_nonfinite(x) ? 0.0 : x;
+      const uint32_t qv = static_cast<uint32_t>(ceil_scaled_abs(x, exponent_of(x), kQBits - f));
+      packed[k >> 2] |= qv << (8 * (k & 3));
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(bbar + static_cast<long>(j) * q_pad + blk * kKPad + 16 * L);
+  *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
+// accu exponents from the bound-product maxima.
+__global__ void accu_exponents_kernel(int na, int nb, const int* __restrict__ e_row,
+                                      const int* __restrict__ f_col, const int* __restrict__ rho,
+                                      const int* __restrict__ gamma, int* __restrict__ d,
+                                      int* __restrict__ b, int tau) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= na + nb) return;
+  const bool is_a = idx < na;
+  const int line = is_a ? idx : idx - na;
+  const int e = is_a ? e_row[line] : f_col[line];
+  const int peak = is_a ? rho[line] : gamma[line];
+  int out = 0;
+  if (e != kNoExp) out = ((tau - clog2_u64(static_cast<uint64_t>(max(peak, 1)))) >> 1) + kQBits - e;
+  if (is_a)
+    d[line] = out;
+  else
+    b[line] = out;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+static inline unsigned blocks_for(long n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
+
+hipError_t launch_fill_i32(int* ptr, int value, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, ptr, value, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, ptr, value, n);
+  return hipGetLastError();
+}
+
+template <bool MAXONLY>
+static hipError_t launch_stats(const double* A, long lda, const double* B, long ldb, const Work& w,
+                               hipStream_t st) {
+  if (w.nch > 0 && w.p > 0) {
+    dim3 grid(blocks_for(w.p, kWave), w.nch);
+    hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(256), 0, st, A, lda, w.p, w.q, w.nch, w.part_e_a,
+                       w.part_s_a, w.flags);
+  }
+  if (w.nch > 0 && w.r > 0) {
+    dim3 grid(w.r, blocks_for(w.nch, 4));
+    hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, B, ldb, w.q, w.r, w.nch, w.part_e_b,
+                       w.part_s_b, w.flags);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_scaling(const double* A, long lda, const double* B, long ldb, const Work& w,
+                               hipStream_t st) {
+  hipError_t e = launch_stats<false>(A, lda, B, ldb, w, st);
+  if (e != hipSuccess) return e;
+  const int n = w.p + w.r;
+  hipLaunchKernelGGL(fast_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.nch,
+                     w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b, w.d, w.b, w.tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_accu_bound_inputs(const double* A, long lda, const double* B, long ldb, const Work& w,
+                                    hipStream_t st) {
+  hipError_t e = launch_stats<true>(A, lda, B, ldb, w, st);
+  if (e != hipSuccess) return e;
+  const int n = w.p + w.r;
+  hipLaunchKernelGGL(max_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.nch,
+                     w.part_e_a, w.part_e_b, w.e_row, w.f_col);
+  const int nblk = w.q_pad / kKPad;
+  if (nblk > 0) {
+    dim3 grid_a(w.p_pad / kWave, nblk * 4);
+    hipLaunchKernelGGL(quant_rows_kernel, grid_a, dim3(256), 0, st, A, lda, w.p, w.q, w.q_pad, w.e_row, w.abar);
+    dim3 grid_b(w.r_pad, blocks_for(nblk, 16));
+    hipLaunchKernelGGL(quant_cols_kernel, grid_b, dim3(256), 0, st, B, ldb, w.q, w.r, w.q_pad, nblk, w.f_col,
+                       w.bbar);
+  }
+  // the bound GEMM accumulates maxima with atomics: start from 0
+  if ((e = launch_fill_i32(w.rho, 0, w.p, st)) != hipSuccess) return e;
+  if ((e = launch_fill_i32(w.gamma, 0, w.r, st)) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_accu_exponents(const Work& w, hipStream_t st) {
+  const int n = w.p + w.r;
+  hipLaunchKernelGGL(accu_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.e_row,
+                     w.f_col, w.rho, w.gamma, w.d, w.b, w.tau);
+  return hipGetLastError();
+}
+
+}  // namespace oz2

@@ -1,0 +1,162 @@
+/*
+ * oz2.h -- C ABI of the Ozaki Scheme II FP64 GEMM emulation for AMD MI355X (gfx950).
+ *
+ * The library computes C ~= A * B for FP64 matrices with s exact INT8 x INT8 -> INT32
+ * modular GEMMs and Chinese-Remainder reconstruction, following the pipeline of
+ * "Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part I section 1 (stage table),
+ * and "Ozaki II supplement: INT8 range conditions and paper performance results",
+ * section 1.1:
+ *
+ *   D, E      power-of-two row / column scalings from a bound (fast or accu)
+ *   A' = trunc(D A),  B' = trunc(B E)
+ *   A_t = rho_{m_t}(A'),  B_t = rho_{m_t}(B')      centered int8 residues, t = 1..s
+ *   P_t = A_t B_t                                  int8 x int8 -> int32, exact for q < 2^17
+ *   R_t = P_t mod m_t                              nonnegative, uint8
+ *   X   = CRT(R_1..R_s) in [-M/2, M/2),  M = prod m_t
+ *   C   = D^-1 X E^-1
+ *
+ * Moduli: the first s pairwise-coprime integers taken greedily downward from 256
+ * (256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223, 217, 211, 199, 197, ...).
+ *
+ * Conventions for every entry point:
+ *   - Matrices are column-major FP64: A is p x q with leading dimension lda >= max(1,p),
+ *     B is q x r with ldb >= max(1,q), C is p x r with ldc >= max(1,p).
+ *   - Matrix and workspace pointers are DEVICE pointers on the current HIP device.
+ *     C must not overlap A, B or the workspace.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *     enqueued asynchronously on it; no entry point synchronizes unless stated.
+ *   - Arguments are validated before anything is enqueued; on an error return nothing
+ *     has been launched and C is untouched.
+ *   - Not thread-safe: calls share one library workspace and one timing state; calls on
+ *     different streams that share a workspace must be ordered by the caller.
+ */
+#ifndef OZ2_H
+#define OZ2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bound used to choose D and E ("Profiling Ozaki II", Part I section 2). */
+typedef enum {
+  OZ2_FAST = 0, /* Cauchy-Schwarz bound from row/column max-abs and sums of squares */
+  OZ2_ACCU = 1  /* positional bound from one extra upward-quantized |A| |B| INT8 GEMM */
+} oz2_mode_t;
+
+/* Status codes returned by every int-valued entry point. */
+enum {
+  OZ2_OK = 0,
+  OZ2_ERR_ARG = 1,         /* invalid size, leading dimension, pointer, s or mode */
+  OZ2_ERR_UNSUPPORTED = 2, /* q >= 2^17: INT32 accumulation no longer provably exact */
+  OZ2_ERR_WORKSPACE = 3,   /* caller workspace too small, or device allocation failed */
+  OZ2_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+};
+
+#define OZ2_MIN_S 2
+#define OZ2_MAX_S 20
+/* Largest inner dimension: q * 128^2 < 2^31 iff q < 2^17 ("Ozaki II supplement", section 1.3). */
+#define OZ2_MAX_Q 131071
+/* X is dumped as a 160-bit two's-complement integer in 5 little-endian 32-bit limbs. */
+#define OZ2_X_LIMBS 5
+
+/* Flag bits reported by ozaki2_get_flags. */
+#define OZ2_FLAG_NONFINITE 1u /* A or B held Inf/NaN; affected entries of C are unspecified */
+
+/*
+ * ozaki2_dgemm -- C = A * B emulated with s INT8 modular GEMMs (the whole pipeline above).
+ *   p, q, r : sizes (>= 0; p == 0 or r == 0 is a no-op; q == 0 writes C = 0).
+ *   s       : number of moduli, OZ2_MIN_S..OZ2_MAX_S.
+ *   mode    : OZ2_FAST or OZ2_ACCU.
+ * Uses the workspace set by ozaki2_set_workspace, else a library-owned device buffer
+ * that is allocated (or grown) on first need and kept until ozaki2_release().
+ * Returns OZ2_OK, OZ2_ERR_ARG, OZ2_ERR_UNSUPPORTED, OZ2_ERR_WORKSPACE or OZ2_ERR_HIP.
+ */
+int ozaki2_dgemm(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
+                 double* C, int ldc, int s, int mode, void* stream);
+
+/* Bytes of device workspace ozaki2_dgemm / ozaki2_dgemm_debug need for these sizes
+ * (0 if the arguments are invalid or describe no work). */
+size_t ozaki2_workspace_size(int p, int q, int r, int s, int mode);
+
+/* Use a caller-owned device buffer (256-byte aligned, `bytes` long) as the workspace.
+ * dev_ptr == NULL reverts to the library-owned buffer.  The caller keeps ownership and
+ * must keep the buffer alive while calls using it are in flight. */
+int ozaki2_set_workspace(void* dev_ptr, size_t bytes);
+
+/* Free the library-owned workspace and timing events (synchronizes the device). */
+int ozaki2_release(void);
+
+/*
+ * Validation dumps for ozaki2_dgemm_debug.  Every member is a device pointer the
+ * caller owns; NULL members are skipped.  Layouts (t = modulus index 0..s-1):
+ *   d[p], b[r]           int32 scaling exponents: D = diag(2^d), E = diag(2^b)
+ *   Ap[p*q]              A' as exact FP64 integers, column-major, ld p
+ *   Bp[q*r]              B' as exact FP64 integers, column-major, ld q
+ *   At[s*p*q]            A_t[i][l] at At[(t*p + i)*q + l]
+ *   Bt[s*r*q]            B_t[l][j] at Bt[(t*r + j)*q + l]
+ *   P[s*r*p]             P_t[i][j] at P[(t*r + j)*p + i]   (int32)
+ *   R[s*r*p]             R_t[i][j] at R[(t*r + j)*p + i]   (uint8)
+ *   X[r*p*5]             X[i][j] at X[(j*p + i)*5 + k], k = 0..4 little-endian limbs
+ * accu mode only (ignored in fast mode):
+ *   e[p], f[r]           max-abs exponents of rows of A / columns of B (E(x): 2^(E-1) <= |x| < 2^E;
+ *                        INT32_MIN for an all-zero line)
+ *   Abar[p*q]            upward-quantized |A|, Abar[i*q + l] in [0, 64]
+ *   Bbar[r*q]            upward-quantized |B|, Bbar[j*q + l] in [0, 64]
+ *   rho[p], gamma[r]     row / column maxima of the bound product Abar * Bbar^T
+ */
+typedef struct oz2_dump {
+  int32_t* d;
+  int32_t* b;
+  double* Ap;
+  double* Bp;
+  int8_t* At;
+  int8_t* Bt;
+  int32_t* P;
+  uint8_t* R;
+  uint32_t* X;
+  int32_t* e;
+  int32_t* f;
+  int8_t* Abar;
+  int8_t* Bbar;
+  int32_t* rho;
+  int32_t* gamma;
+} oz2_dump_t;
+
+/* Same computation and result C as ozaki2_dgemm, also writing every intermediate named
+ * in `dump` (which may be NULL).  Slower (extra kernels and copies); for validation. */
+int ozaki2_dgemm_debug(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
+                       double* C, int ldc, int s, int mode, void* stream, const oz2_dump_t* dump);
+
+/*
+ * Stage timing.  ozaki2_timing_begin(max_calls) pre-creates events for up to max_calls
+ * subsequent ozaki2_dgemm calls; each timed call records HIP events on its stream between
+ * the four stages.  ozaki2_timing_end synchronizes on the last recorded event and returns
+ * the per-stage sums in milliseconds over the timed calls:
+ *   stage_ms[0] scaling   (fast: statistics + exponents; accu: bound inputs, bound GEMM, exponents)
+ *   stage_ms[1] residues  (scale, truncate and all s centered int8 residues of A and B)
+ *   stage_ms[2] gemm      (the batched s INT8 GEMMs with the fused mod-m epilogue)
+ *   stage_ms[3] crt       (CRT reconstruction and inverse scaling into C)
+ * and in *ncalls the number of calls timed.  Timing is then switched off.
+ */
+int ozaki2_timing_begin(int max_calls);
+int ozaki2_timing_end(double* stage_ms, int* ncalls);
+
+/* Synchronizes the stream of the last call and returns its flag word (OZ2_FLAG_*). */
+int ozaki2_get_flags(unsigned* flags);
+
+/* The s moduli used for s (writes s ints) and tau = floor(log2(M/2 - 1)), the
+ * reconstruction budget the scalings keep |(A'B')_ij| <= 2^tau within. */
+int ozaki2_moduli(int s, int* out);
+int ozaki2_tau(int s);
+
+/* Static description of a status code. */
+const char* ozaki2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OZ2_H */

@@ -1,0 +1,125 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and
+compare each intermediate with the CPU oracle on the same seeded inputs."""
+import sys
+
+import numpy as np
+
+import oracle
+
+X_BITS = 32 * 5
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(a_np):
+    import torch
+    from fp64_gemm_emulation_amd import binding
+    t = torch.from_numpy(np.ascontiguousarray(a_np)).cuda()
+    return binding.colmajor(t)
+
+
+def x_limbs_to_int(limbs):
+    """5 little-endian 32-bit limbs (int32 or uint32 values) -> Python int (160-bit two's complement)."""
+    v = 0
+    for k, w in enumerate(limbs):
+        v |= (int(w) & 0xFFFFFFFF) << (32 * k)
+    if v >= 1 << (X_BITS - 1):
+        v -= 1 << X_BITS
+    return v
+
+
+def chat_tolerance(A, B, rows, cols):
+    """4 * 2^-53 * (|A||B|)_ij on the sampled entries (FP64 on the host)."""
+    absab = np.abs(A[rows]) @ np.abs(B[:, cols])
+    return 4.0 * 2.0 ** -53 * absab
+
+
+def assert_chat_close(c_gpu, c_ref, tol, what=""):
+    diff = np.abs(c_gpu - c_ref)
+    bad = diff > tol
+    assert not bad.any(), f"{what}: {bad.sum()} entries out of tolerance, max excess {np.max(diff - tol)}"
+
+
+def compare_full(out, ref, A, B, s, mode):
+    """Every intermediate of a full run, bit-exact; C within the benchmark spec's tolerance."""
+    p, q = A.shape
+    r = B.shape[1]
+    assert np.array_equal(out["d"].cpu().numpy(), ref["d"].astype(np.int32)), "d"
+    assert np.array_equal(out["b"].cpu().numpy(), ref["b"].astype(np.int32)), "b"
+    if mode == "accu":
+        e = np.array([v if v is not None else -(2 ** 31) for v in ref["e"]], dtype=np.int64)
+        f = np.array([v if v is not None else -(2 ** 31) for v in ref["f"]], dtype=np.int64)
+        eg = out["e"].cpu().numpy().astype(np.int64)
+        fg = out["f"].cpu().numpy().astype(np.int64)
+        live_e, live_f = e > -(2 ** 31), f > -(2 ** 31)
+        assert np.array_equal(eg[live_e], e[live_e]) and (eg[~live_e] < -(2 ** 29)).all(), "e"
+        assert np.array_equal(fg[live_f], f[live_f]) and (fg[~live_f] < -(2 ** 29)).all(), "f"
+        assert np.array_equal(out["Abar"].cpu().numpy(), ref["Abar"].astype(np.int8)), "Abar"
+        assert np.array_equal(out["Bbar"].cpu().numpy(), ref["Bbar"].astype(np.int8)), "Bbar"
+        assert np.array_equal(out["rho"].cpu().numpy(), ref["rho"].astype(np.int32)), "rho"
+        assert np.array_equal(out["gamma"].cpu().numpy(), ref["gamma"].astype(np.int32)), "gamma"
+    assert np.array_equal(out["Ap"].cpu().numpy(), ref["Ap"]), "A'"
+    assert np.array_equal(out["Bp"].cpu().numpy(), ref["Bp"]), "B'"
+    at = out["At"].cpu().numpy()
+    bt = out["Bt"].cpu().numpy()
+    pt = out["P"].cpu().numpy()
+    rt = out["R"].cpu().numpy()
+    for t in range(s):
+        assert np.array_equal(at[t], ref["At"][t].astype(np.int8)), f"A_t t={t}"
+        assert np.array_equal(bt[t], ref["Bt"][t].T.astype(np.int8)), f"B_t t={t}"
+        assert np.array_equal(pt[t], ref["P"][t].T.astype(np.int32)), f"P_t t={t}"
+        assert np.array_equal(rt[t], ref["R"][t].T.astype(np.uint8)), f"R_t t={t}"
+    xg = out["X"].cpu().numpy()
+    for j in range(r):
+        for i in range(p):
+            assert x_limbs_to_int(xg[j, i]) == int(ref["X"][i, j]), f"X[{i},{j}]"
+    c = out["C"].cpu().numpy()
+    tol = chat_tolerance(A, B, np.arange(p), np.arange(r))
+    assert_chat_close(c, ref["C"], tol, "C")
+    return int(np.sum(c != ref["C"]))
+
+
+def compare_sampled(out, ref, A, B, s, mode, rows, cols):
+    """Sampled entries of a large run against oracle.ozaki2_sample at (rows, cols)."""
+    d = out["d"][rows].cpu().numpy()
+    b = out["b"][cols].cpu().numpy()
+    assert np.array_equal(d, ref["d"].astype(np.int32)), "d"
+    assert np.array_equal(b, ref["b"].astype(np.int32)), "b"
+    rows_t = __import__("torch").as_tensor(rows, device="cuda")
+    cols_t = __import__("torch").as_tensor(cols, device="cuda")
+    if mode == "accu":
+        assert np.array_equal(out["rho"][rows_t].cpu().numpy(), ref["rho"].astype(np.int32)), "rho"
+        assert np.array_equal(out["gamma"][cols_t].cpu().numpy(), ref["gamma"].astype(np.int32)), "gamma"
+        assert np.array_equal(out["Abar"][rows_t].cpu().numpy(), ref["Abar"].astype(np.int8)), "Abar"
+        assert np.array_equal(out["Bbar"][cols_t].cpu().numpy(), ref["Bbar"].astype(np.int8)), "Bbar"
+    at = out["At"][:, rows_t, :].cpu().numpy()
+    bt = out["Bt"][:, cols_t, :].cpu().numpy()
+    pt = out["P"][:, cols_t][:, :, rows_t].cpu().numpy()
+    rt = out["R"][:, cols_t][:, :, rows_t].cpu().numpy()
+    for t in range(s):
+        assert np.array_equal(at[t], ref["At"][t].astype(np.int8)), f"A_t t={t}"
+        assert np.array_equal(bt[t], ref["Bt"][t].T.astype(np.int8)), f"B_t t={t}"
+        assert np.array_equal(pt[t], ref["P"][t].T.astype(np.int32)), f"P_t t={t}"
+        assert np.array_equal(rt[t], ref["R"][t].T.astype(np.uint8)), f"R_t t={t}"
+    ap = out["Ap"][rows_t].cpu().numpy()
+    bp = out["Bp"][:, cols_t].cpu().numpy()
+    assert np.array_equal(ap, ref["Ap"]), "A'"
+    assert np.array_equal(bp, ref["Bp"]), "B'"
+    xg = out["X"][cols_t][:, rows_t].cpu().numpy()
+    for jj in range(len(cols)):
+        for ii in range(len(rows)):
+            assert x_limbs_to_int(xg[jj, ii]) == int(ref["X"][ii, jj]), f"X[{rows[ii]},{cols[jj]}]"
+    c = out["C"][rows_t][:, cols_t].cpu().numpy()
+    tol = chat_tolerance(A, B, rows, cols)
+    assert_chat_close(c, ref["C"], tol, "C")
+    return int(np.sum(c != ref["C"]))
+
+
+def sample_indices(n, count, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, n // 2, n - 2, n - 1]
+    extra = rng.choice(n, size=min(count, n), replace=False).tolist()
+    return np.array(sorted(set(v for v in fixed + extra if 0 <= v < n)), dtype=np.int64)

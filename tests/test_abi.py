@@ -1,0 +1,101 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the
+header declares, validates arguments on the host before anything is launched, and
+its compile-time constants agree with the oracle's independent derivation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oz2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp64_gemm_emulation_amd import build as b
+    if not os.path.exists(b.LIB_PATH):
+        b.build()
+    from fp64_gemm_emulation_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(ozaki2_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for expected in ["ozaki2_dgemm", "ozaki2_dgemm_debug", "ozaki2_workspace_size", "ozaki2_set_workspace",
+                     "ozaki2_timing_begin", "ozaki2_timing_end", "ozaki2_get_flags", "ozaki2_moduli",
+                     "ozaki2_tau", "ozaki2_status_string", "ozaki2_release"]:
+        assert expected in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_moduli_and_tau_match_oracle(lib):
+    for s in range(oracle.MIN_S, oracle.MAX_S + 1):
+        rc, mods = lib.ozaki2_moduli(s)
+        assert rc == lib.OZ2_OK
+        assert mods == oracle.moduli(s)
+        assert lib.ozaki2_tau(s) == oracle.tau(s)
+    assert lib.ozaki2_moduli(1)[0] == lib.OZ2_ERR_ARG
+    assert lib.ozaki2_moduli(21)[0] == lib.OZ2_ERR_ARG
+    assert lib.ozaki2_tau(21) == -1
+
+
+def test_argument_validation_before_launch(lib):
+    """Invalid arguments return an error before any HIP call (so this runs without a GPU)."""
+    A, B, C = 0x10000, 0x20000000, 0x40000000  # never dereferenced
+    call = lib.ozaki2_dgemm
+    ok = dict(p=8, q=8, r=8, A=A, lda=8, B=B, ldb=8, C=C, ldc=8, s=8, mode=0, stream=None)
+
+    def run(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return call(a["p"], a["q"], a["r"], a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"],
+                    a["s"], a["mode"], a["stream"])
+
+    assert run(s=1) == lib.OZ2_ERR_ARG
+    assert run(s=21) == lib.OZ2_ERR_ARG
+    assert run(mode=2) == lib.OZ2_ERR_ARG
+    assert run(p=-1) == lib.OZ2_ERR_ARG
+    assert run(lda=7) == lib.OZ2_ERR_ARG
+    assert run(ldb=7) == lib.OZ2_ERR_ARG
+    assert run(ldc=7) == lib.OZ2_ERR_ARG
+    assert run(C=None) == lib.OZ2_ERR_ARG
+    assert run(A=None) == lib.OZ2_ERR_ARG
+    assert run(q=131072, ldb=131072) == lib.OZ2_ERR_UNSUPPORTED
+    assert run(C=A + 8) == lib.OZ2_ERR_ARG          # C overlaps A
+    assert run(p=0) == lib.OZ2_OK                     # empty: no work, nothing launched
+    assert run(r=0) == lib.OZ2_OK
+    assert lib.ozaki2_dgemm_debug(8, 8, 8, A, 8, B, 8, C, 8, 1, 0, None, None) == lib.OZ2_ERR_ARG
+
+
+def test_workspace_size(lib):
+    ws = lib.ozaki2_workspace_size
+    assert ws(0, 8, 8, 8, 0) == 0
+    assert ws(8, 8, 8, 1, 0) == 0
+    assert ws(8, 131072, 8, 8, 0) == 0
+    small = ws(100, 100, 100, 8, 0)
+    assert small > 0 and small % 256 == 0
+    assert ws(100, 100, 100, 14, 0) > small
+    # int8 operand planes and residue planes dominate: s (p_pad q_pad + r_pad q_pad + r_pad p_pad)
+    n = 8192
+    assert ws(n, n, n, 14, 0) >= 14 * 3 * n * n
+    assert lib.ozaki2_set_workspace(0x101, 1024) == lib.OZ2_ERR_ARG   # misaligned
+    assert lib.ozaki2_set_workspace(None, 0) == lib.OZ2_OK
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert isinstance(lib.ozaki2_status_string(code), str)
+    assert "unknown" in lib.ozaki2_status_string(99)

@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer intermediates (d, b, A', B', A_t, B_t, P_t, R_t, X and, for accu, e, f, Abar,
+Bbar, rho, gamma) must be bit-exact; the FP64 result C must satisfy
+|C_gpu - C_oracle|_ij <= 4 * 2^-53 * (|A||B|)_ij.  Small and ragged shapes are compared
+in full; the full-size workloads are compared on sampled rows and columns.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp64_gemm_emulation_amd.workloads import WORKLOADS, generate
+from tests.gpu_helpers import (compare_full, compare_sampled, log, sample_indices, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def oz():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    from fp64_gemm_emulation_amd import binding
+    return binding
+
+
+def _full_case(oz, A, B, s, mode, label):
+    log(f"[full] {label}: p,q,r={A.shape[0]},{A.shape[1]},{B.shape[1]} s={s} mode={mode}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode)
+    ref = oracle.ozaki2(A, B, s, mode)
+    ndiff = compare_full(out, ref, A, B, s, mode)
+    log(f"[full] {label}: ok ({ndiff} C entries differ from the correctly rounded value)")
+    return out, ref
+
+
+def test_workload_n256_fast_s8_full(oz):
+    w = WORKLOADS["n256_fast_s8"]
+    A, B = w.inputs()
+    _full_case(oz, A, B, w.s, w.mode, w.name)
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+@pytest.mark.parametrize("shape", [(300, 517, 129), (1, 1, 1), (257, 256, 255), (513, 1000, 70), (5, 2049, 3)])
+def test_ragged_shapes(oz, mode, shape):
+    p, q, r = shape
+    A = generate(p, q, 1.0, 11 + p)
+    B = generate(q, r, 1.0, 12 + r)
+    _full_case(oz, A, B, 14, mode, f"ragged{shape}")
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+@pytest.mark.parametrize("s", list(range(2, 21)))
+def test_every_modulus_count(oz, mode, s):
+    A = generate(70, 300, 1.0, 100 + s)
+    B = generate(300, 45, 1.0, 200 + s)
+    _full_case(oz, A, B, s, mode, f"s{s}")
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_edge_values(oz, mode):
+    A = generate(64, 300, 4.0, 5)          # very wide exponent spread
+    B = generate(300, 40, 4.0, 6)
+    A[3, :] = 0.0                           # zero row
+    B[:, 7] = 0.0                           # zero column
+    A[5, 10] = 5e-324                       # subnormals
+    A[6, :20] = -3e-310
+    B[11, 2] = 1e300                        # huge
+    B[12, 3] = -1e-300
+    A[9, :] = 1.0                           # flat row
+    _full_case(oz, A, B, 14, mode, "edges")
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_small_integers_exact(oz, mode):
+    rng = np.random.default_rng(3)
+    A = rng.integers(-1000, 1001, size=(90, 200)).astype(np.float64)
+    B = rng.integers(-1000, 1001, size=(200, 77)).astype(np.float64)
+    out, ref = _full_case(oz, A, B, 14, mode, "integers")
+    exact = (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float64)
+    assert np.array_equal(out["C"].cpu().numpy(), exact)
+
+
+def test_inner_dimension_zero_gives_zero(oz):
+    import torch
+    A = torch.empty((5, 0), dtype=torch.float64, device="cuda")
+    B = torch.empty((0, 4), dtype=torch.float64, device="cuda")
+    C = oz.empty_colmajor(5, 4)
+    C.fill_(7.0)
+    rc = oz.ozaki2_dgemm(5, 0, 4, 0, 5, 0, 1, C.data_ptr(), 5, 8, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == oz.OZ2_OK
+    torch.cuda.synchronize()
+    assert not C.cpu().numpy().any()
+
+
+def test_nonfinite_flagged(oz):
+    import torch
+    A = generate(40, 64, 0.5, 1)
+    B = generate(64, 30, 0.5, 2)
+    A[3, 4] = np.inf
+    oz.dgemm(to_device(A), to_device(B), 8, "fast")
+    rc, flags = oz.ozaki2_get_flags()
+    assert rc == oz.OZ2_OK and flags & 1
+    oz.dgemm(to_device(generate(40, 64, 0.5, 1)), to_device(B), 8, "fast")
+    rc, flags = oz.ozaki2_get_flags()
+    assert rc == oz.OZ2_OK and flags == 0
+    torch.cuda.synchronize()
+
+
+def test_deterministic_and_leading_dimensions(oz):
+    import torch
+    A = generate(200, 333, 1.0, 7)
+    B = generate(333, 150, 1.0, 8)
+    Ad, Bd = to_device(A), to_device(B)
+    c1 = oz.dgemm(Ad, Bd, 14, "accu")
+    c2 = oz.dgemm(Ad, Bd, 14, "accu")
+    assert torch.equal(c1, c2)
+    # padded leading dimensions give the same result
+    Abig = torch.zeros((333, 256), dtype=torch.float64, device="cuda").t()   # ld 256 > 200
+    Abig[:200, :] = Ad
+    Ap = Abig[:200, :]
+    Bbig = torch.zeros((150, 400), dtype=torch.float64, device="cuda").t()   # ld 400 > 333
+    Bbig[:333, :] = Bd
+    Bp = Bbig[:333, :]
+    Cbig = torch.zeros((150, 300), dtype=torch.float64, device="cuda").t()
+    Cp = Cbig[:200, :]
+    oz.dgemm(Ap, Bp, 14, "accu", out=Cp)
+    torch.cuda.synchronize()
+    assert torch.equal(Cp, c1)
+    assert not Cbig[200:, :].any()
+
+
+def test_caller_workspace_and_timing(oz):
+    import torch
+    A = generate(128, 256, 0.5, 1)
+    B = generate(256, 96, 0.5, 2)
+    Ad, Bd = to_device(A), to_device(B)
+    ref = oz.dgemm(Ad, Bd, 8, "fast")
+    need = oz.ozaki2_workspace_size(128, 256, 96, 8, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert oz.ozaki2_set_workspace(ws.data_ptr(), need) == oz.OZ2_OK
+    try:
+        assert oz.ozaki2_timing_begin(4) == oz.OZ2_OK
+        c = oz.dgemm(Ad, Bd, 8, "fast")
+        c = oz.dgemm(Ad, Bd, 8, "fast")
+        rc, ms, n = oz.ozaki2_timing_end()
+        assert rc == oz.OZ2_OK and n == 2 and all(v >= 0 for v in ms)
+        assert torch.equal(c, ref)
+        with pytest.raises(oz.Oz2Error):
+            oz.dgemm(Ad, Bd, 14, "fast")          # needs more than the caller gave
+        torch.cuda.synchronize()
+    finally:
+        assert oz.ozaki2_set_workspace(None, 0) == oz.OZ2_OK
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled comparison
+# ---------------------------------------------------------------------------
+def _sampled_case(oz, name, nsamp=12):
+    import torch
+    w = WORKLOADS[name]
+    log(f"[sampled] {name}: generating inputs n={w.n}")
+    A, B = w.inputs()
+    want = ("d", "b", "Ap", "Bp", "At", "Bt", "P", "R", "X") + (("rho", "gamma", "Abar", "Bbar") if w.mode == "accu" else ())
+    log(f"[sampled] {name}: GPU run s={w.s} mode={w.mode}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), w.s, w.mode, want=want)
+    torch.cuda.synchronize()
+    rows = sample_indices(w.n, nsamp, 1)
+    cols = sample_indices(w.n, nsamp, 2)
+    log(f"[sampled] {name}: oracle on {len(rows)} rows x {len(cols)} cols")
+    ref = oracle.ozaki2_sample(A, B, w.s, w.mode, rows, cols)
+    ndiff = compare_sampled(out, ref, A, B, w.s, w.mode, rows, cols)
+    if w.mode == "fast" and w.n <= 8192:
+        log(f"[sampled] {name}: full d and b vectors")
+        d_ref, _, _ = oracle.fast_exponents(A, w.s)
+        b_ref, _, _ = oracle.fast_exponents(B.T, w.s)
+        assert np.array_equal(out["d"].cpu().numpy(), d_ref.astype(np.int32))
+        assert np.array_equal(out["b"].cpu().numpy(), b_ref.astype(np.int32))
+    log(f"[sampled] {name}: ok ({ndiff} sampled C entries differ from the correctly rounded value)")
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_workload_n2048_fast_s14(oz):
+    _sampled_case(oz, "n2048_fast_s14", nsamp=24)
+
+
+def test_workload_n8192_fast_s14(oz):
+    _sampled_case(oz, "n8192_fast_s14")
+
+
+def test_workload_n8192_accu_s14(oz):
+    _sampled_case(oz, "n8192_accu_s14")
+
+
+def test_workload_n16384_fast_s18(oz):
+    _sampled_case(oz, "n16384_fast_s18", nsamp=8)
+
+
+def test_workload_n16384_accu_s18(oz):
+    _sampled_case(oz, "n16384_accu_s18", nsamp=8)
