@@ -20,6 +20,8 @@
 // Output layout: A_t[t][i][q_pad], B_t[t][j][q_pad] int8, inner dimension K-permuted in
 // 256-blocks (kperm_pos) so that 16 consecutive bytes belong to one thread; both
 // operands use the same permutation, so every P_t is unchanged.
+#include <algorithm>
+
 #include "oz2_common.hpp"
 #include "oz2_internal.hpp"
 
@@ -234,24 +236,28 @@ hipError_t launch_residues(const double* A, long lda, const double* B, long ldb,
 }
 
 // Validation: src [planes][rows_pad][q_pad] (K-permuted) -> dst [planes][rows][q].
+// Grid-stride loop: the dispatch grid size counts work-items in 32 bits, so the launch is
+// capped and each thread walks the whole range.
 __global__ void unpermute_i8_kernel(const int8_t* __restrict__ src, int rows, int rows_pad, int q, int q_pad,
                                     int8_t* __restrict__ dst, long total) {
-  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int l = static_cast<int>(idx % q);
-  const long rest = idx / q;
-  const int row = static_cast<int>(rest % rows);
-  const long plane = rest / rows;
-  const int pos = (l & ~(kKPad - 1)) + kperm_pos(l & (kKPad - 1));
-  dst[idx] = src[(plane * rows_pad + row) * q_pad + pos];
+  const long stride = static_cast<long>(gridDim.x) * blockDim.x;
+  for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int l = static_cast<int>(idx % q);
+    const long rest = idx / q;
+    const int row = static_cast<int>(rest % rows);
+    const long plane = rest / rows;
+    const int pos = (l & ~(kKPad - 1)) + kperm_pos(l & (kKPad - 1));
+    dst[idx] = src[(plane * rows_pad + row) * q_pad + pos];
+  }
 }
 
 hipError_t launch_unpermute_i8(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
                                int8_t* dst, hipStream_t st) {
   const long total = static_cast<long>(planes) * rows * q;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(unpermute_i8_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, src,
-                     rows, rows_pad, q, q_pad, dst, total);
+  const long blocks = std::min<long>((total + 255) / 256, 1L << 20);
+  hipLaunchKernelGGL(unpermute_i8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, src, rows,
+                     rows_pad, q, q_pad, dst, total);
   return hipGetLastError();
 }
 

@@ -47,31 +47,33 @@ def compare_full(out, ref, A, B, s, mode):
     """Every intermediate of a full run, bit-exact; C within the benchmark spec's tolerance."""
     p, q = A.shape
     r = B.shape[1]
-    assert np.array_equal(out["d"].cpu().numpy(), ref["d"].astype(np.int32)), "d"
-    assert np.array_equal(out["b"].cpu().numpy(), ref["b"].astype(np.int32)), "b"
+    assert_equal(out["d"].cpu().numpy(), ref["d"].astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), ref["b"].astype(np.int32), "b")
     if mode == "accu":
         e = np.array([v if v is not None else -(2 ** 31) for v in ref["e"]], dtype=np.int64)
         f = np.array([v if v is not None else -(2 ** 31) for v in ref["f"]], dtype=np.int64)
         eg = out["e"].cpu().numpy().astype(np.int64)
         fg = out["f"].cpu().numpy().astype(np.int64)
         live_e, live_f = e > -(2 ** 31), f > -(2 ** 31)
-        assert np.array_equal(eg[live_e], e[live_e]) and (eg[~live_e] < -(2 ** 29)).all(), "e"
-        assert np.array_equal(fg[live_f], f[live_f]) and (fg[~live_f] < -(2 ** 29)).all(), "f"
-        assert np.array_equal(out["Abar"].cpu().numpy(), ref["Abar"].astype(np.int8)), "Abar"
-        assert np.array_equal(out["Bbar"].cpu().numpy(), ref["Bbar"].astype(np.int8)), "Bbar"
-        assert np.array_equal(out["rho"].cpu().numpy(), ref["rho"].astype(np.int32)), "rho"
-        assert np.array_equal(out["gamma"].cpu().numpy(), ref["gamma"].astype(np.int32)), "gamma"
-    assert np.array_equal(out["Ap"].cpu().numpy(), ref["Ap"]), "A'"
-    assert np.array_equal(out["Bp"].cpu().numpy(), ref["Bp"]), "B'"
+        assert_equal(eg[live_e], e[live_e], "e")
+        assert (eg[~live_e] < -(2 ** 29)).all(), "e of zero rows"
+        assert_equal(fg[live_f], f[live_f], "f")
+        assert (fg[~live_f] < -(2 ** 29)).all(), "f of zero columns"
+        assert_equal(out["Abar"].cpu().numpy(), ref["Abar"].astype(np.int8), "Abar")
+        assert_equal(out["Bbar"].cpu().numpy(), ref["Bbar"].astype(np.int8), "Bbar")
+        assert_equal(out["rho"].cpu().numpy(), ref["rho"].astype(np.int32), "rho")
+        assert_equal(out["gamma"].cpu().numpy(), ref["gamma"].astype(np.int32), "gamma")
+    assert_equal(out["Ap"].cpu().numpy(), ref["Ap"], "A'")
+    assert_equal(out["Bp"].cpu().numpy(), ref["Bp"], "B'")
     at = out["At"].cpu().numpy()
     bt = out["Bt"].cpu().numpy()
     pt = out["P"].cpu().numpy()
     rt = out["R"].cpu().numpy()
     for t in range(s):
-        assert np.array_equal(at[t], ref["At"][t].astype(np.int8)), f"A_t t={t}"
-        assert np.array_equal(bt[t], ref["Bt"][t].T.astype(np.int8)), f"B_t t={t}"
-        assert np.array_equal(pt[t], ref["P"][t].T.astype(np.int32)), f"P_t t={t}"
-        assert np.array_equal(rt[t], ref["R"][t].T.astype(np.uint8)), f"R_t t={t}"
+        assert_equal(at[t], ref["At"][t].astype(np.int8), f"A_t t={t}")
+        assert_equal(bt[t], ref["Bt"][t].T.astype(np.int8), f"B_t t={t}")
+        assert_equal(pt[t], ref["P"][t].T.astype(np.int32), f"P_t t={t}")
+        assert_equal(rt[t], ref["R"][t].T.astype(np.uint8), f"R_t t={t}")
     xg = out["X"].cpu().numpy()
     for j in range(r):
         for i in range(p):
@@ -95,19 +97,19 @@ def compare_sampled(out, ref, A, B, s, mode, rows, cols):
         assert np.array_equal(out["gamma"][cols_t].cpu().numpy(), ref["gamma"].astype(np.int32)), "gamma"
         assert np.array_equal(out["Abar"][rows_t].cpu().numpy(), ref["Abar"].astype(np.int8)), "Abar"
         assert np.array_equal(out["Bbar"][cols_t].cpu().numpy(), ref["Bbar"].astype(np.int8)), "Bbar"
+    ap = out["Ap"][rows_t].cpu().numpy()
+    bp = out["Bp"][:, cols_t].cpu().numpy()
+    assert_equal(ap, ref["Ap"], "A'")
+    assert_equal(bp, ref["Bp"], "B'")
     at = out["At"][:, rows_t, :].cpu().numpy()
     bt = out["Bt"][:, cols_t, :].cpu().numpy()
     pt = out["P"][:, cols_t][:, :, rows_t].cpu().numpy()
     rt = out["R"][:, cols_t][:, :, rows_t].cpu().numpy()
     for t in range(s):
-        assert np.array_equal(at[t], ref["At"][t].astype(np.int8)), f"A_t t={t}"
-        assert np.array_equal(bt[t], ref["Bt"][t].T.astype(np.int8)), f"B_t t={t}"
-        assert np.array_equal(pt[t], ref["P"][t].T.astype(np.int32)), f"P_t t={t}"
-        assert np.array_equal(rt[t], ref["R"][t].T.astype(np.uint8)), f"R_t t={t}"
-    ap = out["Ap"][rows_t].cpu().numpy()
-    bp = out["Bp"][:, cols_t].cpu().numpy()
-    assert np.array_equal(ap, ref["Ap"]), "A'"
-    assert np.array_equal(bp, ref["Bp"]), "B'"
+        assert_equal(at[t], ref["At"][t].astype(np.int8), f"A_t t={t}")
+        assert_equal(bt[t], ref["Bt"][t].T.astype(np.int8), f"B_t t={t}")
+        assert_equal(pt[t], ref["P"][t].T.astype(np.int32), f"P_t t={t}")
+        assert_equal(rt[t], ref["R"][t].T.astype(np.uint8), f"R_t t={t}")
     xg = out["X"][cols_t][:, rows_t].cpu().numpy()
     for jj in range(len(cols)):
         for ii in range(len(rows)):
@@ -116,6 +118,17 @@ def compare_sampled(out, ref, A, B, s, mode, rows, cols):
     tol = chat_tolerance(A, B, rows, cols)
     assert_chat_close(c, ref["C"], tol, "C")
     return int(np.sum(c != ref["C"]))
+
+
+def assert_equal(got, want, what):
+    """Bit-exact comparison that reports where it fails."""
+    if got.shape == want.shape and np.array_equal(got, want):
+        return
+    if got.shape != want.shape:
+        raise AssertionError(f"{what}: shape {got.shape} != {want.shape}")
+    bad = np.argwhere(got != want)
+    head = ", ".join(f"{tuple(int(v) for v in ix)}: gpu {got[tuple(ix)]} oracle {want[tuple(ix)]}" for ix in bad[:5])
+    raise AssertionError(f"{what}: {len(bad)} of {got.size} entries differ; first: {head}")
 
 
 def sample_indices(n, count, seed):
