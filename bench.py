@@ -11,6 +11,7 @@ average event interval is that kernel's average launch duration.
 Prints one JSON line.  Only one GPU is supported: --gpus above 1 exits with a message.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +26,33 @@ PEAK_INT8_TOPS = 5000.0     # dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0       # HBM3E, GB/s
 # Pages' number for this metric and workload (GH200, fast-14, n = 8192; paper Table 3)
 PAGES_FAST14_N8192_GH200 = 72.1
+
+
+GEMM_SOURCE = os.path.join(ROOT, "fp64_gemm_emulation_amd", "csrc", "oz2_gemm.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, or None.
+
+    The summary records FETCH_SIZE and WRITE_SIZE of the GEMM kernel scaled by the same
+    counters on a plain device copy of known size, and the SHA-256 of the GEMM source it
+    was taken with; a different source means the figure is stale and None is returned.
+    """
+    path = os.path.join(ROOT, "profiles", f"gemm_i8_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if fields.get("gemm_source_sha256") != src_hash:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def stage_bytes(n_p, n_q, n_r, s, accu):
@@ -67,8 +95,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n8192_fast_s14")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=32)
-    ap.add_argument("--cpu-cols", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--cpu-cols", type=int, default=2048)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -91,6 +121,13 @@ def main():
     Bd = binding.colmajor(torch.from_numpy(np.ascontiguousarray(B)).to(dev))
     C = binding.empty_colmajor(n, n, device=dev)
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 27, dtype=torch.float64, device=dev).fill_(1.0)   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
@@ -150,7 +187,7 @@ def main():
             "peak": PEAK_INT8_TOPS,
             "unit": "TFLOP/s",
             "frac": gemm_tops / PEAK_INT8_TOPS,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
         "nonfinite_flag": bool(flags & 1),
     }
