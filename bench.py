@@ -88,6 +88,19 @@ def cpu_baseline(A, B, s, mode, rows, cols):
     }
 
 
+def native_fp64_context(Ad, Bd, n, reps=10):
+    """Native FP64 GEMM of the same operands through torch (vendor library), for context."""
+    import torch
+    Cn = torch.matmul(Ad, Bd)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.matmul(Ad, Bd, out=Cn)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return {"native_fp64_matmul_tflops": 2.0 * n ** 3 / dt / 1e12, "native_fp64_matmul_ms": dt * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,7 +108,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n8192_fast_s14")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--no-context", action="store_true", help="skip the native FP64 matmul context figure")
+    ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--cpu-cols", type=int, default=2048)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
@@ -134,12 +148,16 @@ def main():
     torch.cuda.synchronize()
 
     assert binding.ozaki2_timing_begin(args.steps) == binding.OZ2_OK
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for k in range(args.steps):
         binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
+        marks[k + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
     rc, stage_ms, ncalls = binding.ozaki2_timing_end()
     assert rc == binding.OZ2_OK and ncalls == args.steps
     rc, flags = binding.ozaki2_get_flags()
@@ -162,6 +180,9 @@ def main():
         "gemm_frac_int8_peak": gemm_tops / PEAK_INT8_TOPS,
         "residues_per_s": 2.0 * s * n * n / (st[1] * 1e-3),
         "int8_macs_per_s": s * float(n) ** 3 / (st[2] * 1e-3),
+        "step_ms_median": per_step[len(per_step) // 2],
+        "step_ms_min": per_step[0],
+        "step_ms_max": per_step[-1],
     }
     result = {
         "metric": "effective FP64 TFLOPS (2n^3/t), n=8192 fast-14; per-stage ms breakdown",
@@ -191,6 +212,8 @@ def main():
         },
         "nonfinite_flag": bool(flags & 1),
     }
+    if not args.no_context:
+        result["context"] = native_fp64_context(Ad, Bd, n)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(A, B, s, w.mode, args.cpu_rows, args.cpu_cols)
     else:

@@ -69,11 +69,36 @@ __device__ __forceinline__ int clog2_u64(uint64_t v) {
   return v <= 1 ? 0 : 64 - __clzll(static_cast<long long>(v - 1));
 }
 
-// Position of element l (0 <= l < kKPad within a 256-block) in the K-permuted operand
-// layout: lane L of a 16-lane group owns l = L + 16 k (k = 0..15) and stores them as 16
-// consecutive bytes at 16 L + k.  Any permutation of the inner dimension applied to
-// both operands leaves every P_t unchanged.
-__host__ __device__ __forceinline__ int kperm_pos(int l) { return ((l & 15) << 4) | (l >> 4); }
-__host__ __device__ __forceinline__ int kperm_inv(int pos) { return ((pos & 15) << 4) | (pos >> 4); }
+// Operand planes (A_t, B_t and the accu quantized operands) are stored in the order the
+// GEMM consumes them, tile-contiguous:
+//   [256-row block][64-byte stage of the inner dimension][256 rows x 64 bytes],
+// and inside a row's 64-byte segment the four 16-byte chunks are XOR-swizzled by
+// operand_swizzle(row % 16).  One GEMM stage tile of one operand is then a contiguous
+// 16 KiB block that is copied into LDS unchanged, and 16-byte fragment reads of 16
+// consecutive rows at one logical chunk hit 16 distinct LDS bank groups.
+//
+// Within each 256-long block of the inner dimension the producer thread for "slot" L
+// (0..15) owns the elements l = L + 16 k (k = 0..15) and stores them as one 16-byte chunk,
+// byte k; slot L is logical chunk L % 4 of stage L / 4 of the block.  The same order is
+// used for both operands, and any common permutation of the inner dimension leaves every
+// P_t unchanged.
+constexpr int kStageK = 64;                    // inner-dimension bytes per GEMM stage
+constexpr int kStageTile = kRowPad * kStageK;  // bytes of one operand stage tile (16 KiB)
+
+__host__ __device__ __forceinline__ int operand_swizzle(int r16) { return ((r16 >> 1) ^ (r16 >> 3)) & 3; }
+
+// Byte offset, within one operand plane of q_pad-long rows, of the 16-byte chunk of slot
+// L (0..15) of 256-block blk of row `row`.
+__host__ __device__ __forceinline__ long operand_chunk_offset(int row, int blk, int slot, int q_pad) {
+  const int rr = row & (kRowPad - 1);
+  const long tile = static_cast<long>(row / kRowPad) * (q_pad / kStageK) + blk * (kKPad / kStageK) + (slot >> 2);
+  return tile * kStageTile + rr * kStageK + 16 * ((slot & 3) ^ operand_swizzle(rr & 15));
+}
+
+// Byte offset of inner-dimension element l of row `row` (the inverse map, for validation).
+__host__ __device__ __forceinline__ long operand_elem_offset(int row, int l, int q_pad) {
+  const int w = l & (kKPad - 1);
+  return operand_chunk_offset(row, l / kKPad, w & 15, q_pad) + (w >> 4);
+}
 
 }  // namespace oz2

@@ -6,53 +6,84 @@
 //
 // Exactness: |A_t|, |B_t| <= 128, so every product is at most 2^14 and every partial sum
 // of a length-q dot product stays below q 2^14 < 2^31 for q < 2^17, in any order
-// ("Ozaki II supplement", section 1.3).  Operand planes are int8 with the inner dimension
-// contiguous (and identically K-permuted for both operands), rows padded to 256 and the
-// inner dimension to 256 with zeros, so the kernel needs no bounds checks in the K loop.
+// ("Ozaki II supplement", section 1.3).  Operand planes are int8 in the tile-contiguous
+// layout of operand_chunk_offset (rows padded to 256, the inner dimension to 256 with
+// zeros), so the kernel needs no bounds checks in the K loop.
 #include "oz2_common.hpp"
 #include "oz2_internal.hpp"
 
 namespace oz2 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // Tile: 256 x 256 outputs per workgroup, 4 waves in a 2 x 2 grid, each wave 128 x 128 =
-// 8 x 8 blocks of v_mfma_i32_16x16x64_i8 (256 accumulator registers per lane).
+// 4 x 4 blocks of v_mfma_i32_32x32x32_i8 (256 accumulator registers per lane).  From one
+// wave per SIMD this form keeps the matrix core close to fully busy, where back-to-back
+// 16x16x64 MFMAs reach only about half of it.
 //
-// K advances in stages of 64 bytes.  Operands go from global memory straight into a ring
-// of kStages LDS buffers with global_load_lds_dwordx4 (no staging registers), so up to
-// four stages are in flight and the load latency is covered by several stages of MFMAs.
-// In LDS each 256 x 64-byte operand tile is stored row-major with its four 16-byte
-// chunks XOR-swizzled by bits 2..3 of the row: one load instruction fills 1 KiB
-// contiguously (16 rows), and the 16-byte fragment reads of 16 consecutive rows touch 16
-// distinct bank groups.  Per stage and wave: MFMAs of the first half of the tile rows;
-// wait for the next stage's loads and synchronize; refill the buffer just consumed with
-// the stage four ahead; read the next stage's fragments while the second half's MFMAs
-// run.
+// K advances in stages of 64 bytes (two 32-deep halves).  Each stage tile of each operand
+// is a contiguous 16 KiB block in memory, copied into a ring of kStages LDS buffers with
+// global_load_lds_dwordx4 (1 KiB per instruction, no staging registers).  Per stage and
+// wave:
+//   first half:  wait for this half's fragments; 16 MFMAs, with the 8 fragment reads of
+//                the second half issued among the first 8;
+//   middle:      wait for the next stage's copies and the fragments; barrier;
+//   second half: 16 MFMAs, with the copy of stage kt + 4 into the buffer just released
+//                and the 8 first-half fragment reads of stage kt + 1 among the first 8.
+// At most 8 LDS reads are ever outstanding, so every wait is an exact count, and each
+// wait falls where the data has had half a stage of MFMAs to arrive.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 64;
+constexpr int kBK = kStageK;                    // 64 bytes of the inner dimension per stage
 constexpr int kStages = 4;
-constexpr int kTileBytes = kBM * kBK;          // 16 KiB per operand per stage
-constexpr int kStageBytes = 2 * kTileBytes;    // A then B
-constexpr int kLoadsPerStage = 8;              // global_load_lds per wave per stage (4 A + 4 B)
+constexpr int kTileBytes = kStageTile;          // 16 KiB per operand per stage
+constexpr int kStageBytes = 2 * kTileBytes;     // A then B
+constexpr int kLoadsPerStage = 8;               // global_load_lds per wave per stage (4 A + 4 B)
 constexpr int kGroupM = 4;  // tile rows per group of the XCD-aware launch order
+static_assert(kBM == kRowPad && kBN == kRowPad, "operand stage tiles are 256 rows");
 
-// Constants of the output reduction R = P mod m for each modulus (index t):
-// c16 = 2^16 mod m, inv = RN(1/m) in FP32.
+// Constants of the output reduction R = P mod m for each modulus (index t).  The
+// accumulators start at -h (h = (m - 1) / 2 for odd m, 0 for m = 256), so the epilogue
+// sees P' = P - h:
+//   z = (P' mod 2^16) + (P' >> 16) c16 with c16 the centered residue of 2^16, computed as
+//       one v_mad_i32_i24 with the multiplier c16 - 2^16; |z| < 2^22.02 and z = P' (mod m);
+//   y = RN(z / m + magic) in FP32 gives magic + round(z / m) exactly (z / m is never within
+//       1/(2m) of a half-integer and the FP32 quotient is within 0.26/m of it);
+//   z - m (low 24 bits of y) = [z - m round(z / m)] - m 2^22 + m e, and with
+//       magic = 1.5 2^23 - e, e = h m^-1 (mod 256), its low byte is
+//       centered residue of P' + h = P mod m, in [0, m).
 struct ModRed {
   int m;
-  int c16;
-  float inv;
+  int h;
+  int c16m;      // centered (2^16 mod m) - 2^16
+  float inv;     // RN(1 / m)
+  float magic;   // 1.5 2^23 - e
 };
+
+constexpr int half_of(int m) { return (m & 1) ? (m - 1) / 2 : 0; }
+constexpr int shift_e(int m) {
+  return (m & 1) ? static_cast<int>((static_cast<uint32_t>(half_of(m)) * inv_mod(static_cast<uint32_t>(m) & 255u, 256u)) & 255u)
+                 : 0;
+}
+constexpr ModRed mod_red(int t) {
+  return ModRed{modulus(t), half_of(modulus(t)),
+                centered_small(pow2_mod(16, static_cast<uint32_t>(modulus(t))), static_cast<uint32_t>(modulus(t))) - 65536,
+                1.0f / static_cast<float>(modulus(t)), 12582912.0f - static_cast<float>(shift_e(modulus(t)))};
+}
+constexpr bool mod_red_ok() {
+  for (int t = 0; t < kMaxS; ++t) {
+    const int m = modulus(t);
+    if ((m & 1) && (m * shift_e(m)) % 256 != half_of(m)) return false;
+  }
+  return true;
+}
+static_assert(mod_red_ok(), "m e = h (mod 256) for every odd modulus");
+
 __constant__ ModRed kModRed[kMaxS] = {
-#define OZ2_MR(T) {modulus(T), static_cast<int>(pow2_mod(16, modulus(T))), 1.0f / static_cast<float>(modulus(T))}
-    OZ2_MR(0),  OZ2_MR(1),  OZ2_MR(2),  OZ2_MR(3),  OZ2_MR(4),  OZ2_MR(5),  OZ2_MR(6),
-    OZ2_MR(7),  OZ2_MR(8),  OZ2_MR(9),  OZ2_MR(10), OZ2_MR(11), OZ2_MR(12), OZ2_MR(13),
-    OZ2_MR(14), OZ2_MR(15), OZ2_MR(16), OZ2_MR(17), OZ2_MR(18), OZ2_MR(19)
-#undef OZ2_MR
-};
+    mod_red(0),  mod_red(1),  mod_red(2),  mod_red(3),  mod_red(4),  mod_red(5),  mod_red(6),
+    mod_red(7),  mod_red(8),  mod_red(9),  mod_red(10), mod_red(11), mod_red(12), mod_red(13),
+    mod_red(14), mod_red(15), mod_red(16), mod_red(17), mod_red(18), mod_red(19)};
 
 __device__ __forceinline__ int mad_i24(int a, int b, int c) {
   int d;
@@ -60,17 +91,11 @@ __device__ __forceinline__ int mad_i24(int a, int b, int c) {
   return d;
 }
 
-// P mod m in [0, m) for |P| < 2^31, 2 <= m <= 256.  For odd m: P = a 2^16 + b gives
-// z = a (2^16 mod m) + b = P (mod m) with |z| < 2^23, so round(z / m) is exact from one
-// FP32 FMA (z / m is never within 1/(2m) of a half-integer), and z - m round(z/m) is
-// the centered residue, moved to [0, m).
-__device__ __forceinline__ uint32_t mod_nonneg(int P, const ModRed& mr) {
-  if (mr.m == 256) return static_cast<uint32_t>(P) & 0xFFu;
-  const int z = mad_i24(P >> 16, mr.c16, P & 0xFFFF);
-  const float y = __builtin_fmaf(static_cast<float>(z), mr.inv, 12582912.0f);
-  int r = mad_i24(__float_as_int(y), -mr.m, z) + (mr.m << 22);  // low 24 bits of y: 2^22 + round(z/m)
-  r += (r >> 31) & mr.m;
-  return static_cast<uint32_t>(r);
+// Low byte = P mod m for an accumulator holding P' = P - h (odd m); see ModRed.
+__device__ __forceinline__ uint32_t mod_byte(int pp, const ModRed& mr) {
+  const int z = mad_i24(pp >> 16, mr.c16m, pp);
+  const float y = __builtin_fmaf(static_cast<float>(z), mr.inv, mr.magic);
+  return static_cast<uint32_t>(mad_i24(__float_as_int(y), -mr.m, z));
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Give
@@ -89,9 +114,11 @@ __device__ __forceinline__ void tile_coords(unsigned wg, int tiles_m, int tiles_
   tj = static_cast<int>(in_group / gm);
 }
 
-// s_waitcnt with only the vector-memory counter constrained: vmcnt <= N (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
+// s_waitcnt with one counter constrained (gfx9 encoding: vmcnt bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]; the others left at their maxima).
 #define OZ2_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (((N) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+#define OZ2_WAIT_LGKMCNT(N) __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (((N) & 0xF) << 8))
+#define OZ2_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -115,154 +142,171 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
   tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
   const int i0 = tile_i * kBM;
   const int j0 = tile_j * kBN;
-
-  // DMA: wave w fills rows [64 w + 16 j, +16) of each operand tile, j = 0..3; lane l
-  // lands at row 16 j + l / 4, physical chunk l % 4, and so fetches logical chunk
-  // (l % 4) ^ ((l / 16) % 4) of that row.  Uniform bases live in SGPRs; each lane keeps
-  // one 32-bit offset (a tile spans at most 256 rows of K < 2^17 bytes).
-  const int8_t* const ga = at + t * a_plane + static_cast<long>(i0 + 64 * wave) * K;
-  const int8_t* const gb = bt + t * b_plane + static_cast<long>(j0 + 64 * wave) * K;
-  const unsigned loff = static_cast<unsigned>((lane >> 2) * K + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
-  auto dma = [&](int kbuf, int ksrc) {
-    int8_t* sa = smem + (kbuf % kStages) * kStageBytes + wave * 64 * kBK;
-    const long k0 = static_cast<long>(ksrc) * kBK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long rowk = static_cast<long>(16 * j) * K + k0;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ga + rowk + loff),
-                                       (lds_ptr_t)(sa + j * 16 * kBK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(gb + rowk + loff),
-                                       (lds_ptr_t)(sa + kTileBytes + j * 16 * kBK), 16, 0, 0);
-    }
-  };
-
-  // fragment reads: row R = 128 w + 16 blk + lane % 16, logical chunk lane / 16
-  const int fofs = (lane & 15) * kBK + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
-  const int8_t* const fa0 = smem + wm * 128 * kBK + fofs;
-  const int8_t* const fb0 = smem + kTileBytes + wn * 128 * kBK + fofs;
-
-  v4i acc[8][8];
-#pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4i{0, 0, 0, 0};
-
-  v4i fa0r[8], fb0r[8], fa1r[8], fb1r[8];
-  auto lread_b = [&](int kt, v4i (&xb)[8]) {
-    const int buf = (kt % kStages) * kStageBytes;
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) xb[ni] = *reinterpret_cast<const v4i*>(fb0 + buf + ni * 16 * kBK);
-  };
-  auto lread_a = [&](int kt, v4i (&xa)[8], int m_lo) {
-    const int buf = (kt % kStages) * kStageBytes;
-#pragma unroll
-    for (int mi = m_lo; mi < m_lo + 4; ++mi) xa[mi] = *reinterpret_cast<const v4i*>(fa0 + buf + mi * 16 * kBK);
-  };
-  auto mfma_rows = [&](const v4i (&xa)[8], const v4i (&xb)[8], int m_lo) {
-#pragma unroll
-    for (int mi = m_lo; mi < m_lo + 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 8; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[mi], xb[ni], acc[mi][ni], 0, 0, 0);
-  };
-  auto sync = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-  };
-
-  // K / kBK is a multiple of 4 (the inner dimension is padded to 256), so the stage loop
-  // runs in pairs and needs no tail.  The body is branch-free: the refill for stage
-  // kt + 4 is always issued, from stage min(kt + 4, nk - 1), into the buffer of stage kt,
-  // which nothing reads after the barrier; so exactly two stages of loads are always
-  // outstanding behind the one the next barrier needs.
   const int nk = K / kBK;
-  // one stage: MFMAs of rows 0..3 with the current fragments; wait for stage kt + 1 and
-  // synchronize; refill the buffer of stage kt; read stage kt + 1's B fragments and rows
-  // 0..3 of its A fragments; MFMAs of rows 4..7; read rows 4..7 of stage kt + 1's A
-  // fragments (covered by the next stage's first half).
-  auto stage = [&](int kt, v4i (&ca)[8], v4i (&cb)[8], v4i (&na)[8], v4i (&nb)[8]) {
-    mfma_rows(ca, cb, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    OZ2_WAIT_VMCNT(2 * kLoadsPerStage);
-    sync();
-    dma(kt, min(kt + 4, nk - 1));
-    lread_b(kt + 1, nb);
-    lread_a(kt + 1, na, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_rows(ca, cb, 4);
-    lread_a(kt + 1, na, 4);
+
+  // Copies: wave w moves bytes [4096 w + 1024 g, +1024) of each 16 KiB stage tile (g =
+  // 0..3 for A, again for B); lane l lands at byte 16 l of that KiB.
+  const int8_t* const ga = at + t * a_plane + static_cast<long>(tile_i) * kBM * K + wave * 4096 + 16 * lane;
+  const int8_t* const gb = bt + t * b_plane + static_cast<long>(tile_j) * kBN * K + wave * 4096 + 16 * lane;
+  auto copy1 = [&](int kbuf, int ksrc, int g) {
+    const long src = static_cast<long>(ksrc) * kTileBytes + (g & 3) * 1024;
+    int8_t* dst = smem + (kbuf % kStages) * kStageBytes + wave * 4096 + (g & 3) * 1024;
+    if (g < 4)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ga + src), (lds_ptr_t)dst, 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(gb + src), (lds_ptr_t)(dst + kTileBytes), 16, 0, 0);
+  };
+
+  // Accumulators start at -h for the mod epilogues (see ModRed), at 0 for the bound.
+  int init = 0;
+  if constexpr (EPI != kEpiBound) init = -kModRed[t].h;
+  v16i acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = init;
+
+  // Fragment of a 32-row block for one 32-deep half: lane l reads row 32 blk + l % 32,
+  // logical 16-byte chunk 2 half + l / 32 (the same for A and B, so the K positions that
+  // one MFMA pairs up agree).  f0 holds the first half's 4 A and 4 B fragments, f1 the
+  // second half's.
+  const int frow = lane & 31;
+  const int fsw = operand_swizzle(frow & 15);
+  const int fk = lane >> 5;
+  const int8_t* const fa = smem + wm * 128 * kBK + frow * kBK;
+  const int8_t* const fb = smem + kTileBytes + wn * 128 * kBK + frow * kBK;
+  v4i f0[8], f1[8];
+  auto read1 = [&](int kbuf, int half, v4i (&x)[8], int g) {
+    const int off = (kbuf % kStages) * kStageBytes + 16 * ((2 * half + fk) ^ fsw);
+    if (g < 4) x[g] = *reinterpret_cast<const v4i*>(fa + off + g * 32 * kBK);
+    else x[g] = *reinterpret_cast<const v4i*>(fb + off + (g - 4) * 32 * kBK);
+  };
+  // MFMA pair g (0..7) of a half: blocks (g / 2, 2 (g % 2)) and (g / 2, 2 (g % 2) + 1)
+  auto mfma2 = [&](const v4i (&x)[8], int g) {
+    const int mb = g >> 1, nb = 2 * (g & 1);
+    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[mb], x[4 + nb], acc[mb][nb], 0, 0, 0);
+    acc[mb][nb + 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[mb], x[5 + nb], acc[mb][nb + 1], 0, 0, 0);
   };
 
   if (nk > 0) {
-    // prologue: stages 0..3 in flight (clamped for short K), wait for stage 0
+    // Prologue: stages 0..3 in flight (clamped to the last stage for short K), wait for
+    // stage 0, read its first-half fragments.
 #pragma unroll
-    for (int kt = 0; kt < kStages; ++kt) dma(kt, min(kt, nk - 1));
+    for (int kt = 0; kt < kStages; ++kt)
+#pragma unroll
+      for (int g = 0; g < kLoadsPerStage; ++g) copy1(kt, min(kt, nk - 1), g);
     OZ2_WAIT_VMCNT(3 * kLoadsPerStage);
-    sync();
-    lread_b(0, fb0r);
-    lread_a(0, fa0r, 0);
-    lread_a(0, fa0r, 4);
-    for (int kt = 0; kt < nk; kt += 2) {
-      stage(kt, fa0r, fb0r, fa1r, fb1r);
-      stage(kt + 1, fa1r, fb1r, fa0r, fb0r);
+    __builtin_amdgcn_s_barrier();
+    OZ2_SCHED_FENCE();
+#pragma unroll
+    for (int g = 0; g < 8; ++g) read1(0, 0, f0, g);
+    OZ2_SCHED_FENCE();
+    // The body is branch-free: the copy for stage kt + 4 is always issued, from stage
+    // min(kt + 4, nk - 1), into the buffer of stage kt, which nothing reads after the
+    // middle barrier; so exactly two younger stages of copies are outstanding when a
+    // stage's copies are waited for.  Past the last stage, the first-half reads fetch a
+    // buffer that is not used again.
+    for (int kt = 0; kt < nk; ++kt) {
+      OZ2_WAIT_LGKMCNT(0);
+      OZ2_SCHED_FENCE();
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        mfma2(f0, g);
+        if (g < 4) {
+          read1(kt, 1, f1, 2 * g);
+          read1(kt, 1, f1, 2 * g + 1);
+        }
+        OZ2_SCHED_FENCE();
+      }
+      OZ2_WAIT_VMCNT(2 * kLoadsPerStage);
+      OZ2_WAIT_LGKMCNT(0);
+      OZ2_SCHED_FENCE();
+      __builtin_amdgcn_s_barrier();
+      OZ2_SCHED_FENCE();
+      const int kn = min(kt + kStages, nk - 1);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        mfma2(f1, g);
+        if (g < 4) {
+          copy1(kt, kn, 2 * g);
+          copy1(kt, kn, 2 * g + 1);
+          read1(kt + 1, 0, f0, 2 * g);
+          read1(kt + 1, 0, f0, 2 * g + 1);
+        }
+        OZ2_SCHED_FENCE();
+      }
     }
-    // no LDS DMA may still be in flight when the workgroup's LDS is released
+    // no LDS copy may still be in flight when the workgroup's LDS is released
     OZ2_WAIT_VMCNT(0);
+    OZ2_WAIT_LGKMCNT(0);
   }
 
-  // acc[mi][ni][v] holds P_t[i][j] with
-  //   i = i0 + 128 wm + 16 mi + 4 (lane / 16) + v,   j = j0 + 128 wn + 16 ni + lane % 16.
-  const int ib = i0 + wm * 128 + 4 * (lane >> 4);
-  const int jb = j0 + wn * 128 + (lane & 15);
+  // acc[mb][nb][v] holds P_t[i][j] (minus h in the mod epilogues) with
+  //   i = i0 + 128 wm + 32 mb + 8 (v / 4) + 4 (lane / 32) + v % 4,
+  //   j = j0 + 128 wn + 32 nb + lane % 32.
+  const int ib = i0 + wm * 128 + 4 * (lane >> 5);
+  const int jb = j0 + wn * 128 + (lane & 31);
   if constexpr (EPI == kEpiBound) {
-    // rows: max over this wave's 128 columns, then over the 16 lanes sharing lane / 16
+    // rows: max over this wave's 128 columns, then over the 32 lanes sharing lane / 32
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
+    for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int v = 0; v < 16; ++v) {
         int mx = 0;
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) mx = max(mx, acc[mi][ni][v]);
+        for (int nb = 0; nb < 4; ++nb) mx = max(mx, acc[mb][nb][v]);
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, kWave));
-        const int i = ib + mi * 16 + v;
-        if ((lane & 15) == 0 && i < p) atomicMax(rho + i, mx);
+        for (int off = 16; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, kWave));
+        const int i = ib + mb * 32 + 8 * (v >> 2) + (v & 3);
+        if ((lane & 31) == 0 && i < p) atomicMax(rho + i, mx);
       }
     }
     // columns: max over this wave's 128 rows
 #pragma unroll
-    for (int ni = 0; ni < 8; ++ni) {
+    for (int nb = 0; nb < 4; ++nb) {
       int mx = 0;
 #pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
-        mx = max(mx, max(max(acc[mi][ni][0], acc[mi][ni][1]), max(acc[mi][ni][2], acc[mi][ni][3])));
-      mx = max(mx, __shfl_xor(mx, 16, kWave));
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = max(mx, acc[mb][nb][v]);
       mx = max(mx, __shfl_xor(mx, 32, kWave));
-      const int j = jb + ni * 16;
-      if (lane < 16 && j < r) atomicMax(gamma + j, mx);
+      const int j = jb + nb * 32;
+      if (lane < 32 && j < r) atomicMax(gamma + j, mx);
     }
   } else {
     const ModRed mr = kModRed[t];
     uint8_t* rt = res + t * r_plane;
+    const bool m256 = mr.m == 256;
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
+    for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-      for (int ni = 0; ni < 8; ++ni) {
-        const int i = ib + mi * 16;
-        const int j = jb + ni * 16;
-        const v4i a4 = acc[mi][ni];
-        const uint32_t r01 = __builtin_amdgcn_perm(mod_nonneg(a4[1], mr), mod_nonneg(a4[0], mr), 0x0c0c0400u);
-        const uint32_t r23 = __builtin_amdgcn_perm(mod_nonneg(a4[3], mr), mod_nonneg(a4[2], mr), 0x0c0c0400u);
-        *reinterpret_cast<uint32_t*>(rt + static_cast<long>(j) * ldr + i) = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
-        if constexpr (EPI == kEpiRawMod) {
-          if (j < r) {
-            int32_t* dst = p_dump + (static_cast<long>(t) * r + j) * p;
+      for (int nb = 0; nb < 4; ++nb) {
+        const int j = jb + nb * 32;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (i + v < p) dst[i + v] = a4[v];
+        for (int g = 0; g < 4; ++g) {
+          const int i = ib + mb * 32 + 8 * g;
+          uint32_t b0 = static_cast<uint32_t>(acc[mb][nb][4 * g]);
+          uint32_t b1 = static_cast<uint32_t>(acc[mb][nb][4 * g + 1]);
+          uint32_t b2 = static_cast<uint32_t>(acc[mb][nb][4 * g + 2]);
+          uint32_t b3 = static_cast<uint32_t>(acc[mb][nb][4 * g + 3]);
+          if (!m256) {  // m = 256: P mod 256 is the low byte of P (h = 0)
+            b0 = mod_byte(static_cast<int>(b0), mr);
+            b1 = mod_byte(static_cast<int>(b1), mr);
+            b2 = mod_byte(static_cast<int>(b2), mr);
+            b3 = mod_byte(static_cast<int>(b3), mr);
+          }
+          const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+          const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+          *reinterpret_cast<uint32_t*>(rt + static_cast<long>(j) * ldr + i) = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+          if constexpr (EPI == kEpiRawMod) {
+            if (j < r) {
+              int32_t* dst = p_dump + (static_cast<long>(t) * r + j) * p;
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (i + v < p) dst[i + v] = acc[mb][nb][4 * g + v] + mr.h;
+            }
           }
         }
       }

@@ -17,9 +17,9 @@
 //   * m = 256 is the low byte of the signed low limb.
 // No FP64 arithmetic and no integer division run inside the modulus loop.
 //
-// Output layout: A_t[t][i][q_pad], B_t[t][j][q_pad] int8, inner dimension K-permuted in
-// 256-blocks (kperm_pos) so that 16 consecutive bytes belong to one thread; both
-// operands use the same permutation, so every P_t is unchanged.
+// Output layout: planes A_t[t] (p_pad x q_pad) and B_t[t] (r_pad x q_pad, one row per
+// column of B) int8, tile-contiguous for the GEMM (operand_chunk_offset); each thread
+// stores 16 residues of one row as one 16-byte chunk.
 #include <algorithm>
 
 #include "oz2_common.hpp"
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(const double* __rest
       if (ok) ap_dump[i + static_cast<long>(col) * p] = apv;
     }
   }
-  store_residues<S, NLHI, 0>(l, at + static_cast<long>(i) * q_pad + blk * kKPad + 16 * L, plane);
+  store_residues<S, NLHI, 0>(l, at + operand_chunk_offset(i, blk, L, q_pad), plane);
 }
 
 // Columns of column-major B (contiguous): 16-lane groups, one per (column j, 256-block);
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __rest
       if (ok) bp_dump[row + static_cast<long>(j) * q] = bpv;
     }
   }
-  store_residues<S, NLHI, 0>(l, bt + static_cast<long>(j) * q_pad + blk * kKPad + 16 * L, plane);
+  store_residues<S, NLHI, 0>(l, bt + operand_chunk_offset(j, blk, L, q_pad), plane);
 }
 
 template <int S, bool ACCU, bool DUMP>
@@ -235,7 +235,8 @@ hipError_t launch_residues(const double* A, long lda, const double* B, long ldb,
   return hipGetLastError();
 }
 
-// Validation: src [planes][rows_pad][q_pad] (K-permuted) -> dst [planes][rows][q].
+// Validation: src planes of rows_pad x q_pad bytes in the tile-contiguous operand layout
+// -> dst [planes][rows][q], plain row-major.
 // Grid-stride loop: the dispatch grid size counts work-items in 32 bits, so the launch is
 // capped and each thread walks the whole range.
 __global__ void unpermute_i8_kernel(const int8_t* __restrict__ src, int rows, int rows_pad, int q, int q_pad,
@@ -246,8 +247,7 @@ __global__ void unpermute_i8_kernel(const int8_t* __restrict__ src, int rows, in
     const long rest = idx / q;
     const int row = static_cast<int>(rest % rows);
     const long plane = rest / rows;
-    const int pos = (l & ~(kKPad - 1)) + kperm_pos(l & (kKPad - 1));
-    dst[idx] = src[(plane * rows_pad + row) * q_pad + pos];
+    dst[idx] = src[plane * rows_pad * q_pad + operand_elem_offset(row, l, q_pad)];
   }
 }
 

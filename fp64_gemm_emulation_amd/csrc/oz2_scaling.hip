@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const double* __restric
       packed[k >> 2] |= qv << (8 * (k & 3));
     }
   }
-  uint4* dst = reinterpret_cast<uint4*>(abar + static_cast<long>(i) * q_pad + blk * kKPad + 16 * L);
+  uint4* dst = reinterpret_cast<uint4*>(abar + operand_chunk_offset(i, blk, L, q_pad));
   *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const double* __restric
       packed[k >> 2] |= qv << (8 * (k & 3));
     }
   }
-  uint4* dst = reinterpret_cast<uint4*>(bbar + static_cast<long>(j) * q_pad + blk * kKPad + 16 * L);
+  uint4* dst = reinterpret_cast<uint4*>(bbar + operand_chunk_offset(j, blk, L, q_pad));
   *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
