@@ -101,6 +101,34 @@ def native_fp64_context(Ad, Bd, n, reps=10):
     return {"native_fp64_matmul_tflops": 2.0 * n ** 3 / dt / 1e12, "native_fp64_matmul_ms": dt * 1e3}
 
 
+def mfma_ceiling(blocks=1024, rounds=3584, reps=5):
+    """Register-only i8 MFMA rate on random, changing operands (libozcalib.so), TOP/s.
+
+    The default size matches the MFMA work of one n = 8192, s = 14 GEMM launch.  Under the
+    board's power limit this is the practical ceiling of a GEMM on residues."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp64_gemm_emulation_amd", "libozcalib.so"))
+    lib.oz2calib_mfma_i8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.oz2calib_mfma_i8.restype = ctypes.c_int
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (blocks * 8 * 256 * 4,), dtype=torch.int32, device="cuda", generator=gen)
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: lib.oz2calib_mfma_i8(src.data_ptr(), blocks, rounds, out.data_ptr(), stream.cuda_stream)
+    assert call() == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ops = blocks * 4 * 16 * 32768 * 2.0 * rounds
+    return ops / (ms * 1e-3) / 1e12
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n8192_fast_s14")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-context", action="store_true", help="skip the native FP64 matmul context figure")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context figures (native FP64 matmul, MFMA ceiling on random operands)")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--cpu-cols", type=int, default=2048)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -213,7 +242,11 @@ def main():
         "nonfinite_flag": bool(flags & 1),
     }
     if not args.no_context:
-        result["context"] = native_fp64_context(Ad, Bd, n)
+        ctx = native_fp64_context(Ad, Bd, n)
+        ceil_tops = mfma_ceiling()
+        ctx["mfma_i8_ceiling_random_operands_tops"] = ceil_tops
+        ctx["gemm_frac_of_mfma_ceiling"] = gemm_tops / ceil_tops
+        result["context"] = ctx
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(A, B, s, w.mode, args.cpu_rows, args.cpu_cols)
     else:

@@ -1,8 +1,9 @@
-"""Build the HIP library ``liboz2.so`` for gfx950 in-tree.
+"""Build the HIP libraries for gfx950 in-tree.
 
 Each ``csrc/*.hip`` file is compiled to an object with hipcc in parallel, then the
-objects are linked into ``fp64_gemm_emulation_amd/liboz2.so``.  Packed FP32
-instructions are disabled for all device code.
+objects are linked into ``fp64_gemm_emulation_amd/liboz2.so`` (the library).  The
+measurement aid ``calib/mfma_ceiling.hip`` becomes ``libozcalib.so``, loaded only by
+bench.py.  Packed FP32 instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -16,6 +17,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "liboz2.so")
+CALIB_SRC = os.path.join(PKG_DIR, "calib", "mfma_ceiling.hip")
+CALIB_LIB = os.path.join(PKG_DIR, "libozcalib.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -53,8 +56,14 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    tmp = CALIB_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", "-o", tmp, CALIB_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CALIB_SRC}:\n{res.stderr}")
+    os.replace(tmp, CALIB_LIB)
     if verbose:
-        print(f"built {LIB_PATH}", file=sys.stderr)
+        print(f"built {LIB_PATH} and {CALIB_LIB}", file=sys.stderr)
     return LIB_PATH
 
 

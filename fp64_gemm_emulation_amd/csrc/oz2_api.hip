@@ -117,9 +117,10 @@ int validate(int p, int q, int r, const double* A, int lda, const double* B, int
   if (mode != OZ2_FAST && mode != OZ2_ACCU) return OZ2_ERR_ARG;
   if (p < 0 || q < 0 || r < 0 || p > kMaxDim || r > kMaxDim) return OZ2_ERR_ARG;
   if (q > OZ2_MAX_Q) return OZ2_ERR_UNSUPPORTED;
-  // one GEMM launch covers every 128 x 128 output tile: keep its work-item count in 32 bits
-  if (static_cast<uint64_t>(round_up(std::max(p, 1), oz2::kRowPad) / 128) *
-          static_cast<uint64_t>(round_up(std::max(r, 1), oz2::kRowPad) / 128) * 256u >= (1ull << 32))
+  // one GEMM launch puts every 256 x 256 output tile of a plane along grid x (256
+  // work-items each): keep that work-item count in 32 bits
+  if (static_cast<uint64_t>(round_up(std::max(p, 1), oz2::kRowPad) / oz2::kRowPad) *
+          static_cast<uint64_t>(round_up(std::max(r, 1), oz2::kRowPad) / oz2::kRowPad) * 256u >= (1ull << 32))
     return OZ2_ERR_UNSUPPORTED;
   if (lda < std::max(1, p) || ldb < std::max(1, q) || ldc < std::max(1, p)) return OZ2_ERR_ARG;
   if (p == 0 || r == 0) return OZ2_OK;

@@ -95,6 +95,36 @@ __host__ __device__ __forceinline__ long operand_chunk_offset(int row, int blk, 
   return tile * kStageTile + rr * kStageK + 16 * ((slot & 3) ^ operand_swizzle(rr & 15));
 }
 
+// Thread mappings of the kernels that produce operand planes, chosen so that each 16-byte
+// chunk store instruction of a wave writes whole cache lines of the layout above.
+struct ChunkOwner {
+  int row;   // operand row (a row of A, or a column of B)
+  int blk;   // 256-block of the inner dimension
+  int slot;  // chunk slot 0..15 within the block
+};
+
+// Rows of column-major A: workgroup = 64 rows x one 64-byte stage, grid (p_pad / 64,
+// q_pad / 64).  Lane l of wave w owns row 16 w + l / 4 and physical chunk l % 4 of that
+// row's stage segment: a store instruction writes 1 KiB contiguous (16 rows x 64 bytes),
+// and a load instruction for one k reads 4 columns x 16 consecutive rows.
+__device__ __forceinline__ ChunkOwner owner_rows_of_a() {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int stage = blockIdx.y;
+  const int row = blockIdx.x * 64 + wave * 16 + (lane >> 2);
+  return ChunkOwner{row, stage >> 2, 4 * (stage & 3) + ((lane & 3) ^ operand_swizzle(row & 15))};
+}
+
+// Columns of column-major B: workgroup = 16 columns x one 256-block, grid (r_pad / 16,
+// q_pad / 256).  Lane l of wave w owns column 4 w + l / 16 and slot l % 16: a load
+// instruction for one k reads 4 runs of 128 contiguous bytes, a store instruction writes
+// 4 runs of 256 contiguous bytes (4 rows x 64 bytes in each of the 4 stage tiles).
+__device__ __forceinline__ ChunkOwner owner_cols_of_b() {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  return ChunkOwner{static_cast<int>(blockIdx.x) * 16 + wave * 4 + (lane >> 4), static_cast<int>(blockIdx.y), lane & 15};
+}
+
 // Byte offset of inner-dimension element l of row `row` (the inverse map, for validation).
 __host__ __device__ __forceinline__ long operand_elem_offset(int row, int l, int q_pad) {
   const int w = l & (kKPad - 1);

@@ -29,7 +29,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 //   first half:  wait for this half's fragments; 16 MFMAs, with the 8 fragment reads of
 //                the second half issued among the first 8;
 //   middle:      wait for the next stage's copies and the fragments; barrier;
-//   second half: 16 MFMAs, with the copy of stage kt + 4 into the buffer just released
+//   second half: 16 MFMAs, with the copy of stage kt + kStages into the buffer just released
 //                and the 8 first-half fragment reads of stage kt + 1 among the first 8.
 // At most 8 LDS reads are ever outstanding, so every wait is an exact count, and each
 // wait falls where the data has had half a stage of MFMAs to arrive.
@@ -191,22 +191,22 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
   };
 
   if (nk > 0) {
-    // Prologue: stages 0..3 in flight (clamped to the last stage for short K), wait for
-    // stage 0, read its first-half fragments.
+    // Prologue: stages 0..kStages-1 in flight (clamped to the last stage for short K),
+    // wait for stage 0, read its first-half fragments.
 #pragma unroll
     for (int kt = 0; kt < kStages; ++kt)
 #pragma unroll
       for (int g = 0; g < kLoadsPerStage; ++g) copy1(kt, min(kt, nk - 1), g);
-    OZ2_WAIT_VMCNT(3 * kLoadsPerStage);
+    OZ2_WAIT_VMCNT((kStages - 1) * kLoadsPerStage);
     __builtin_amdgcn_s_barrier();
     OZ2_SCHED_FENCE();
 #pragma unroll
     for (int g = 0; g < 8; ++g) read1(0, 0, f0, g);
     OZ2_SCHED_FENCE();
-    // The body is branch-free: the copy for stage kt + 4 is always issued, from stage
-    // min(kt + 4, nk - 1), into the buffer of stage kt, which nothing reads after the
-    // middle barrier; so exactly two younger stages of copies are outstanding when a
-    // stage's copies are waited for.  Past the last stage, the first-half reads fetch a
+    // The body is branch-free: the copy for stage kt + kStages is always issued, from
+    // stage min(kt + kStages, nk - 1), into the buffer of stage kt, which nothing reads
+    // after the middle barrier; so exactly kStages - 2 younger stages of copies are
+    // outstanding when a stage's copies are waited for.  Past the last stage, the first-half reads fetch a
     // buffer that is not used again.
     for (int kt = 0; kt < nk; ++kt) {
       OZ2_WAIT_LGKMCNT(0);
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
         }
         OZ2_SCHED_FENCE();
       }
-      OZ2_WAIT_VMCNT(2 * kLoadsPerStage);
+      OZ2_WAIT_VMCNT((kStages - 2) * kLoadsPerStage);
       OZ2_WAIT_LGKMCNT(0);
       OZ2_SCHED_FENCE();
       __builtin_amdgcn_s_barrier();

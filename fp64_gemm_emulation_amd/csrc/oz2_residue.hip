@@ -126,22 +126,20 @@ __device__ __forceinline__ void store_residues(const int (&l)[16][NLHI + 1], int
   }
 }
 
-// Rows of column-major A (lane = row i, coalesced loads along i).  Workgroup: 64 rows x
-// 4 of the 16 lane-slots L of one 256-block; thread covers l = 256 blk + L + 16 k.
+// Rows of column-major A; thread mapping owner_rows_of_a (the thread's 16 elements of
+// row i are l = 256 blk + L + 16 k).
 template <int S, int NLHI, bool DUMP>
 __global__ __launch_bounds__(256) void residues_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
                                                             const int* __restrict__ dsc, int8_t* __restrict__ at,
                                                             long plane, int q_pad, double* __restrict__ ap_dump) {
-  const int lane = threadIdx.x & 63;
-  const int L = (blockIdx.y & 3) * 4 + (threadIdx.x >> 6);
-  const int blk = blockIdx.y >> 2;
-  const int i = blockIdx.x * kWave + lane;
+  const ChunkOwner own = owner_rows_of_a();
+  const int i = own.row;
   const bool row_ok = i < p;
   const int scale = row_ok ? dsc[i] : 0;
   int l[16][NLHI + 1];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int col = blk * kKPad + L + 16 * k;
+    const int col = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = row_ok && col < q;
     const double x = ok ? A[i + static_cast<long>(col) * lda] : 0.0;
     double apv;
@@ -150,29 +148,23 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(const double* __rest
       if (ok) ap_dump[i + static_cast<long>(col) * p] = apv;
     }
   }
-  store_residues<S, NLHI, 0>(l, at + operand_chunk_offset(i, blk, L, q_pad), plane);
+  store_residues<S, NLHI, 0>(l, at + operand_chunk_offset(i, own.blk, own.slot, q_pad), plane);
 }
 
-// Columns of column-major B (contiguous): 16-lane groups, one per (column j, 256-block);
-// lane L covers l = 256 blk + L + 16 k, so each load instruction reads 128 contiguous
-// bytes per group and each store writes 256 contiguous bytes per group.
+// Columns of column-major B (each column contiguous); thread mapping owner_cols_of_b.
 template <int S, int NLHI, bool DUMP>
 __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                             const int* __restrict__ bsc, int8_t* __restrict__ bt,
-                                                            long plane, int q_pad, int nblk,
-                                                            double* __restrict__ bp_dump) {
-  // grid: x = column j, y = groups of 16 consecutive 256-blocks of that column
-  const int L = threadIdx.x & 15;
-  const int blk = blockIdx.y * 16 + (threadIdx.x >> 4);
-  if (blk >= nblk) return;
-  const int j = blockIdx.x;
+                                                            long plane, int q_pad, double* __restrict__ bp_dump) {
+  const ChunkOwner own = owner_cols_of_b();
+  const int j = own.row;
   const bool col_ok = j < r;
   const int scale = col_ok ? bsc[j] : 0;
   const double* col = B + static_cast<long>(col_ok ? j : 0) * ldb;
   int l[16][NLHI + 1];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int row = blk * kKPad + L + 16 * k;
+    const int row = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = col_ok && row < q;
     const double x = ok ? col[row] : 0.0;
     double bpv;
@@ -181,7 +173,7 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __rest
       if (ok) bp_dump[row + static_cast<long>(j) * q] = bpv;
     }
   }
-  store_residues<S, NLHI, 0>(l, bt + operand_chunk_offset(j, blk, L, q_pad), plane);
+  store_residues<S, NLHI, 0>(l, bt + operand_chunk_offset(j, own.blk, own.slot, q_pad), plane);
 }
 
 template <int S, bool ACCU, bool DUMP>
@@ -190,12 +182,12 @@ static void launch_residues_t(const double* A, long lda, const double* B, long l
   constexpr int NL = nl_hi(S, ACCU);
   const int nblk = w.q_pad / kKPad;
   if (nblk == 0) return;
-  dim3 grid_a(w.p_pad / kWave, nblk * 4);
+  dim3 grid_a(w.p_pad / 64, w.q_pad / kStageK);
   hipLaunchKernelGGL((residues_rows_kernel<S, NL, DUMP>), grid_a, dim3(256), 0, st, A, lda, w.p, w.q, w.d, w.at,
                      static_cast<long>(w.p_pad) * w.q_pad, w.q_pad, dump.ap);
-  dim3 grid_b(w.r_pad, (nblk + 15) / 16);
+  dim3 grid_b(w.r_pad / 16, nblk);
   hipLaunchKernelGGL((residues_cols_kernel<S, NL, DUMP>), grid_b, dim3(256), 0, st, B, ldb, w.q, w.r, w.b, w.bt,
-                     static_cast<long>(w.r_pad) * w.q_pad, w.q_pad, nblk, dump.bp);
+                     static_cast<long>(w.r_pad) * w.q_pad, w.q_pad, dump.bp);
 }
 
 template <int S>

@@ -177,15 +177,13 @@ __global__ void max_exponents_kernel(int na, int nb, int nch, const int* __restr
 }
 
 // accu bound inputs of the rows of A: Abar_il = ceil(|a_il| 2^(kQBits - e_i)) in [0, 64],
-// written in the K-permuted operand layout [p_pad][q_pad] (zeros in the padding).
-// Workgroup: 64 rows (lane) x 4 lanes-of-16 L; thread covers l = 256 blk + L + 16 k.
+// written in the tile-contiguous operand layout (zeros in the padding); thread mapping
+// owner_rows_of_a, the thread covers l = 256 blk + L + 16 k.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
                                                          int q_pad, const int* __restrict__ e_row,
                                                          int8_t* __restrict__ abar) {
-  const int lane = threadIdx.x & 63;
-  const int L = (blockIdx.y & 3) * 4 + (threadIdx.x >> 6);
-  const int blk = blockIdx.y >> 2;
-  const int i = blockIdx.x * kWave + lane;
+  const ChunkOwner own = owner_rows_of_a();
+  const int i = own.row, blk = own.blk, L = own.slot;
   const bool row_ok = i < p;
   const int e = row_ok ? e_row[i] : kNoExp;
   uint32_t packed[4] = {0u, 0u, 0u, 0u};
@@ -203,15 +201,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const double* __restric
   *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
-// accu bound inputs of the columns of B (contiguous): groups of 16 lanes per 256-block.
+// accu bound inputs of the columns of B (each column contiguous); thread mapping
+// owner_cols_of_b.
 __global__ __launch_bounds__(256) void quant_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
-                                                         int q_pad, int nblk, const int* __restrict__ f_col,
+                                                         int q_pad, const int* __restrict__ f_col,
                                                          int8_t* __restrict__ bbar) {
-  // grid: x = column j, y = groups of 16 consecutive 256-blocks
-  const int L = threadIdx.x & 15;
-  const int blk = blockIdx.y * 16 + (threadIdx.x >> 4);
-  if (blk >= nblk) return;
-  const int j = blockIdx.x;
+  const ChunkOwner own = owner_cols_of_b();
+  const int j = own.row, blk = own.blk, L = own.slot;
   const bool col_ok = j < r;
   const int f = col_ok ? f_col[j] : kNoExp;
   uint32_t packed[4] = {0u, 0u, 0u, 0u};
@@ -301,11 +297,10 @@ hipError_t launch_accu_bound_inputs(const double* A, long lda, const double* B, 
                      w.part_e_a, w.part_e_b, w.e_row, w.f_col);
   const int nblk = w.q_pad / kKPad;
   if (nblk > 0) {
-    dim3 grid_a(w.p_pad / kWave, nblk * 4);
+    dim3 grid_a(w.p_pad / 64, w.q_pad / kStageK);
     hipLaunchKernelGGL(quant_rows_kernel, grid_a, dim3(256), 0, st, A, lda, w.p, w.q, w.q_pad, w.e_row, w.abar);
-    dim3 grid_b(w.r_pad, blocks_for(nblk, 16));
-    hipLaunchKernelGGL(quant_cols_kernel, grid_b, dim3(256), 0, st, B, ldb, w.q, w.r, w.q_pad, nblk, w.f_col,
-                       w.bbar);
+    dim3 grid_b(w.r_pad / 16, nblk);
+    hipLaunchKernelGGL(quant_cols_kernel, grid_b, dim3(256), 0, st, B, ldb, w.q, w.r, w.q_pad, w.f_col, w.bbar);
   }
   // the bound GEMM accumulates maxima with atomics: start from 0
   if ((e = launch_fill_i32(w.rho, 0, w.p, st)) != hipSuccess) return e;
