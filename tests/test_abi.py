@@ -99,3 +99,16 @@ def test_status_strings(lib):
     for code in range(5):
         assert isinstance(lib.ozaki2_status_string(code), str)
     assert "unknown" in lib.ozaki2_status_string(99)
+
+
+def test_calibration_library_exports_entry_point(lib):
+    """bench.py's MFMA-ceiling aid is a separate library: built beside liboz2.so, with its
+    entry point exported and its argument checks answering without a launch."""
+    from fp64_gemm_emulation_amd import build as b
+    assert os.path.exists(b.CALIB_LIB)
+    calib = ctypes.CDLL(b.CALIB_LIB)
+    fn = calib.oz2calib_mfma_i8
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    assert fn(None, 1, 1, None, None) == 1
+    assert fn(ctypes.c_void_p(16), 0, 1, ctypes.c_void_p(16), None) == 1
