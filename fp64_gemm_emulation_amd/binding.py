@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG_DIR, "liboz2.so")
 
 OZ2_FAST, OZ2_ACCU = 0, 1
 OZ2_OK, OZ2_ERR_ARG, OZ2_ERR_UNSUPPORTED, OZ2_ERR_WORKSPACE, OZ2_ERR_HIP = 0, 1, 2, 3, 4
-OZ2_MIN_S, OZ2_MAX_S, OZ2_MAX_Q, OZ2_X_LIMBS = 2, 20, 131071, 5
+OZ2_MIN_S, OZ2_MAX_S, OZ2_MAX_Q, OZ2_MAX_Q_P_DUMP, OZ2_X_LIMBS = 2, 20, 524287, 131071, 5
+OZ2_OP_N, OZ2_OP_T = 0, 1
 OZ2_FLAG_NONFINITE = 1
 MODES = {"fast": OZ2_FAST, "accu": OZ2_ACCU}
 
@@ -43,6 +44,7 @@ def _load():
     i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     sig = {
         "ozaki2_dgemm": (i, [i, i, i, vp, i, vp, i, vp, i, i, i, vp]),
+        "ozaki2_dgemm_ex": (i, [i, i, i, i, i, ctypes.c_double, vp, i, vp, i, ctypes.c_double, vp, i, i, i, vp]),
         "ozaki2_dgemm_debug": (i, [i, i, i, vp, i, vp, i, vp, i, i, i, vp, ctypes.POINTER(OZ2Dump)]),
         "ozaki2_workspace_size": (sz, [i, i, i, i, i]),
         "ozaki2_set_workspace": (i, [vp, sz]),
@@ -67,6 +69,10 @@ _LIB = _load()
 # --- entry points with the C names -------------------------------------------------
 def ozaki2_dgemm(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream) -> int:
     return _LIB.ozaki2_dgemm(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream)
+
+
+def ozaki2_dgemm_ex(transa, transb, p, q, r, alpha, A, lda, B, ldb, beta, C, ldc, s, mode, stream) -> int:
+    return _LIB.ozaki2_dgemm_ex(transa, transb, p, q, r, alpha, A, lda, B, ldb, beta, C, ldc, s, mode, stream)
 
 
 def ozaki2_dgemm_debug(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream, dump: OZ2Dump | None) -> int:
@@ -158,6 +164,28 @@ def dgemm(A, B, s: int = 14, mode: str = "fast", out=None, stream=None):
                       C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode], _stream_ptr(stream))
     if rc != OZ2_OK:
         raise Oz2Error(rc, "ozaki2_dgemm")
+    return C
+
+
+def dgemm_ex(A, B, transa: bool = False, transb: bool = False, alpha: float = 1.0, beta: float = 0.0,
+             C=None, s: int = 14, mode: str = "fast", stream=None):
+    """C = alpha op(A) op(B) + beta C for column-major CUDA tensors (op = transpose when
+    transa / transb); C is created (and beta must be 0) when not given.  Returns C."""
+    p, q = (A.shape[1], A.shape[0]) if transa else tuple(A.shape)
+    q2, r = (B.shape[1], B.shape[0]) if transb else tuple(B.shape)
+    if q != q2:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = empty_colmajor(p, r, device=A.device)
+    if tuple(C.shape) != (p, r):
+        raise ValueError("C has the wrong shape")
+    rc = ozaki2_dgemm_ex(OZ2_OP_T if transa else OZ2_OP_N, OZ2_OP_T if transb else OZ2_OP_N, p, q, r, float(alpha),
+                         A.data_ptr(), _colmajor_ld(A, "A"), B.data_ptr(), _colmajor_ld(B, "B"), float(beta),
+                         C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode], _stream_ptr(stream))
+    if rc != OZ2_OK:
+        raise Oz2Error(rc, "ozaki2_dgemm_ex")
     return C
 
 

@@ -111,26 +111,47 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
 }
 
-int validate(int p, int q, int r, const double* A, int lda, const double* B, int ldb, const double* C, int ldc,
-             int s, int mode) {
-  if (s < OZ2_MIN_S || s > OZ2_MAX_S) return OZ2_ERR_ARG;
-  if (mode != OZ2_FAST && mode != OZ2_ACCU) return OZ2_ERR_ARG;
-  if (p < 0 || q < 0 || r < 0 || p > kMaxDim || r > kMaxDim) return OZ2_ERR_ARG;
-  if (q > OZ2_MAX_Q) return OZ2_ERR_UNSUPPORTED;
+// One call: C (p x r) = alpha op(A) op(B) + beta C, op(A) p x q, op(B) q x r.
+struct Call {
+  int transa, transb;
+  int p, q, r;
+  double alpha;
+  const double* A;
+  int lda;
+  const double* B;
+  int ldb;
+  double beta;
+  double* C;
+  int ldc;
+  int s, mode;
+};
+
+int validate(const Call& c, const oz2_dump_t* dump) {
+  if (c.s < OZ2_MIN_S || c.s > OZ2_MAX_S) return OZ2_ERR_ARG;
+  if (c.mode != OZ2_FAST && c.mode != OZ2_ACCU) return OZ2_ERR_ARG;
+  if ((c.transa != OZ2_OP_N && c.transa != OZ2_OP_T) || (c.transb != OZ2_OP_N && c.transb != OZ2_OP_T))
+    return OZ2_ERR_ARG;
+  if (c.p < 0 || c.q < 0 || c.r < 0 || c.p > kMaxDim || c.r > kMaxDim) return OZ2_ERR_ARG;
+  if (c.q > OZ2_MAX_Q) return OZ2_ERR_UNSUPPORTED;
+  // the raw P_t dump holds int32 products, exact only without K-blocking
+  if (dump != nullptr && dump->P != nullptr && c.q > OZ2_MAX_Q_P_DUMP) return OZ2_ERR_UNSUPPORTED;
   // one GEMM launch puts every 256 x 256 output tile of a plane along grid x (256
   // work-items each): keep that work-item count in 32 bits
-  if (static_cast<uint64_t>(round_up(std::max(p, 1), oz2::kRowPad) / oz2::kRowPad) *
-          static_cast<uint64_t>(round_up(std::max(r, 1), oz2::kRowPad) / oz2::kRowPad) * 256u >= (1ull << 32))
+  if (static_cast<uint64_t>(round_up(std::max(c.p, 1), oz2::kRowPad) / oz2::kRowPad) *
+          static_cast<uint64_t>(round_up(std::max(c.r, 1), oz2::kRowPad) / oz2::kRowPad) * 256u >= (1ull << 32))
     return OZ2_ERR_UNSUPPORTED;
-  if (lda < std::max(1, p) || ldb < std::max(1, q) || ldc < std::max(1, p)) return OZ2_ERR_ARG;
-  if (p == 0 || r == 0) return OZ2_OK;
-  if (C == nullptr) return OZ2_ERR_ARG;
-  if (q > 0 && (A == nullptr || B == nullptr)) return OZ2_ERR_ARG;
-  const size_t c_bytes = sizeof(double) * (static_cast<size_t>(ldc) * (r - 1) + p);
-  if (q > 0) {
-    const size_t a_bytes = sizeof(double) * (static_cast<size_t>(lda) * (q - 1) + p);
-    const size_t b_bytes = sizeof(double) * (static_cast<size_t>(ldb) * (r - 1) + q);
-    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes)) return OZ2_ERR_ARG;
+  // stored shapes: A is p x q (N) or q x p (T); B is q x r (N) or r x q (T)
+  const int a_rows = c.transa == OZ2_OP_N ? c.p : c.q, a_cols = c.transa == OZ2_OP_N ? c.q : c.p;
+  const int b_rows = c.transb == OZ2_OP_N ? c.q : c.r, b_cols = c.transb == OZ2_OP_N ? c.r : c.q;
+  if (c.lda < std::max(1, a_rows) || c.ldb < std::max(1, b_rows) || c.ldc < std::max(1, c.p)) return OZ2_ERR_ARG;
+  if (c.p == 0 || c.r == 0) return OZ2_OK;
+  if (c.C == nullptr) return OZ2_ERR_ARG;
+  if (c.q > 0 && (c.A == nullptr || c.B == nullptr)) return OZ2_ERR_ARG;
+  const size_t c_bytes = sizeof(double) * (static_cast<size_t>(c.ldc) * (c.r - 1) + c.p);
+  if (c.q > 0) {
+    const size_t a_bytes = sizeof(double) * (static_cast<size_t>(c.lda) * (a_cols - 1) + a_rows);
+    const size_t b_bytes = sizeof(double) * (static_cast<size_t>(c.ldb) * (b_cols - 1) + b_rows);
+    if (overlaps(c.C, c_bytes, c.A, a_bytes) || overlaps(c.C, c_bytes, c.B, b_bytes)) return OZ2_ERR_ARG;
   }
   return OZ2_OK;
 }
@@ -203,10 +224,10 @@ int copy_rows_2d(void* dst, size_t dpitch, const void* src, size_t spitch, size_
   return OZ2_OK;
 }
 
-int run(int p, int q, int r, const double* A, int lda, const double* B, int ldb, double* C, int ldc, int s, int mode,
-        void* stream, const oz2_dump_t* dump) {
-  int rc = validate(p, q, r, A, lda, B, ldb, C, ldc, s, mode);
+int run(const Call& c, void* stream, const oz2_dump_t* dump) {
+  int rc = validate(c, dump);
   if (rc != OZ2_OK) return rc;
+  const int p = c.p, q = c.q, r = c.r, s = c.s, mode = c.mode;
   if (p == 0 || r == 0) return OZ2_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool accu = mode == OZ2_ACCU;
@@ -226,11 +247,14 @@ int run(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
   Recorder rec(st);
   OZ2_TRY(rec.mark(0));
   OZ2_TRY(oz2::launch_fill_u32(w.flags, 0u, 1, st));
+  // rows of op(A) are contiguous when A is transposed; columns of op(B) unless B is
+  const oz2::Operand opa{c.A, c.lda, c.transa == OZ2_OP_T};
+  const oz2::Operand opb{c.B, c.ldb, c.transb == OZ2_OP_N};
   // --- scaling ---
   if (!accu) {
-    OZ2_TRY(oz2::launch_fast_scaling(A, lda, B, ldb, w, st));
+    OZ2_TRY(oz2::launch_fast_scaling(opa, opb, w, st));
   } else {
-    OZ2_TRY(oz2::launch_accu_bound_inputs(A, lda, B, ldb, w, st));
+    OZ2_TRY(oz2::launch_accu_bound_inputs(opa, opb, w, st));
     if (dz.Abar != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.abar, 1, p, w.p_pad, q, w.q_pad, dz.Abar, st));
     if (dz.Bbar != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.bbar, 1, r, w.r_pad, q, w.q_pad, dz.Bbar, st));
     OZ2_TRY(oz2::launch_gemm(w, 2, dp, st));
@@ -245,7 +269,7 @@ int run(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
   if (dz.b != nullptr) OZ2_TRY(hipMemcpyAsync(dz.b, w.b, sizeof(int) * r, hipMemcpyDeviceToDevice, st));
   OZ2_TRY(rec.mark(1));
   // --- residues ---
-  OZ2_TRY(oz2::launch_residues(A, lda, B, ldb, w, dp, st));
+  OZ2_TRY(oz2::launch_residues(opa, opb, w, dp, st));
   if (dz.At != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.at, s, p, w.p_pad, q, w.q_pad, dz.At, st));
   if (dz.Bt != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.bt, s, r, w.r_pad, q, w.q_pad, dz.Bt, st));
   OZ2_TRY(rec.mark(2));
@@ -260,7 +284,7 @@ int run(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
   }
   OZ2_TRY(rec.mark(3));
   // --- CRT + inverse scaling ---
-  OZ2_TRY(oz2::launch_crt(w, C, ldc, dp, st));
+  OZ2_TRY(oz2::launch_crt(w, c.C, c.ldc, c.alpha, c.beta, dp, st));
   OZ2_TRY(rec.mark(4));
   g.last_stream = st;
   g.last_flags = w.flags;
@@ -273,12 +297,20 @@ extern "C" {
 
 int ozaki2_dgemm(int p, int q, int r, const double* A, int lda, const double* B, int ldb, double* C, int ldc, int s,
                  int mode, void* stream) {
-  return run(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream, nullptr);
+  const Call c{OZ2_OP_N, OZ2_OP_N, p, q, r, 1.0, A, lda, B, ldb, 0.0, C, ldc, s, mode};
+  return run(c, stream, nullptr);
+}
+
+int ozaki2_dgemm_ex(int transa, int transb, int p, int q, int r, double alpha, const double* A, int lda,
+                    const double* B, int ldb, double beta, double* C, int ldc, int s, int mode, void* stream) {
+  const Call c{transa, transb, p, q, r, alpha, A, lda, B, ldb, beta, C, ldc, s, mode};
+  return run(c, stream, nullptr);
 }
 
 int ozaki2_dgemm_debug(int p, int q, int r, const double* A, int lda, const double* B, int ldb, double* C, int ldc,
                        int s, int mode, void* stream, const oz2_dump_t* dump) {
-  return run(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream, dump);
+  const Call c{OZ2_OP_N, OZ2_OP_N, p, q, r, 1.0, A, lda, B, ldb, 0.0, C, ldc, s, mode};
+  return run(c, stream, dump);
 }
 
 size_t ozaki2_workspace_size(int p, int q, int r, int s, int mode) {

@@ -10,7 +10,8 @@
 // away from a half-integer, far above its FP64 rounding error (< 2^-35).  The limbs are
 // carried into a two's-complement multiword integer and converted to FP64 with one
 // round-to-nearest-even, then scaled by 2^-(d_i + b_j) with ldexp (exact unless the
-// result is subnormal).
+// result is subnormal).  The stored value is alpha Chat when beta = 0 (C is not read) and
+// fma(alpha, Chat, RN(beta C)) otherwise, so alpha = 1, beta = 0 stores Chat itself.
 #include "oz2_common.hpp"
 #include "oz2_internal.hpp"
 
@@ -63,7 +64,7 @@ template <int S, bool DUMPX>
 __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ res, long r_plane, int ldr, int p,
                                                   int r, int groups, const int* __restrict__ d,
                                                   const int* __restrict__ b, double* __restrict__ C, long ldc,
-                                                  uint32_t* __restrict__ x_dump) {
+                                                  double alpha, double beta, uint32_t* __restrict__ x_dump) {
   constexpr int L = CrtTable<S>::L;
   // grid: x = column j, y = blocks of 256 row groups
   const int j = blockIdx.x;
@@ -133,6 +134,14 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ re
     out[v] = neg ? -mag : mag;
   }
   double* dst = C + i0 + static_cast<long>(j) * ldc;
+  if (beta != 0.0) {
+#pragma unroll
+    for (int v = 0; v < kRowsPerThread; ++v)
+      if (i0 + v < p) out[v] = fma(alpha, out[v], beta * dst[v]);
+  } else if (alpha != 1.0) {
+#pragma unroll
+    for (int v = 0; v < kRowsPerThread; ++v) out[v] *= alpha;
+  }
   if (i0 + kRowsPerThread <= p && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
     typedef double v2d __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -145,34 +154,37 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ re
 }
 
 template <int S>
-static void launch_crt_s(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st) {
+static void launch_crt_s(const Work& w, double* C, long ldc, double alpha, double beta, const DumpPtrs& dump,
+                         hipStream_t st) {
   const int groups = (w.p + kRowsPerThread - 1) / kRowsPerThread;
   if (groups == 0 || w.r == 0) return;
   const dim3 blocks(w.r, (groups + 255) / 256);
   const long r_plane = static_cast<long>(w.r_pad) * w.p_pad;
   if (dump.x != nullptr)
     hipLaunchKernelGGL((crt_kernel<S, true>), blocks, dim3(256), 0, st, w.res, r_plane, w.p_pad, w.p, w.r,
-                       groups, w.d, w.b, C, ldc, dump.x);
+                       groups, w.d, w.b, C, ldc, alpha, beta, dump.x);
   else
     hipLaunchKernelGGL((crt_kernel<S, false>), blocks, dim3(256), 0, st, w.res, r_plane, w.p_pad, w.p, w.r,
-                       groups, w.d, w.b, C, ldc, nullptr);
+                       groups, w.d, w.b, C, ldc, alpha, beta, nullptr);
 }
 
 template <int S>
-static bool dispatch_crt(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st) {
+static bool dispatch_crt(const Work& w, double* C, long ldc, double alpha, double beta, const DumpPtrs& dump,
+                         hipStream_t st) {
   if constexpr (S > kMaxS) {
     return false;
   } else {
     if (w.s == S) {
-      launch_crt_s<S>(w, C, ldc, dump, st);
+      launch_crt_s<S>(w, C, ldc, alpha, beta, dump, st);
       return true;
     }
-    return dispatch_crt<S + 1>(w, C, ldc, dump, st);
+    return dispatch_crt<S + 1>(w, C, ldc, alpha, beta, dump, st);
   }
 }
 
-hipError_t launch_crt(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st) {
-  if (!dispatch_crt<kMinS>(w, C, ldc, dump, st)) return hipErrorInvalidValue;
+hipError_t launch_crt(const Work& w, double* C, long ldc, double alpha, double beta, const DumpPtrs& dump,
+                      hipStream_t st) {
+  if (!dispatch_crt<kMinS>(w, C, ldc, alpha, beta, dump, st)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

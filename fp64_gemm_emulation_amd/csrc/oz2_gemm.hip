@@ -6,7 +6,12 @@
 //
 // Exactness: |A_t|, |B_t| <= 128, so every product is at most 2^14 and every partial sum
 // of a length-q dot product stays below q 2^14 < 2^31 for q < 2^17, in any order
-// ("Ozaki II supplement", section 1.3).  Operand planes are int8 in the tile-contiguous
+// ("Ozaki II supplement", section 1.3).  Longer inner dimensions run as successive
+// launches over K-blocks of kKBlock bytes; each later block adds the previous block's
+// residues in its epilogue (kEpiModAcc: R_t <- (P_block + R_t) mod m_t).  A block of
+// kKBlock = 2^17 is exact: for odd m the residues are at most 127 in magnitude
+// (2^17 127^2 < 2^31), and for m = 256 only the low byte is used, which INT32
+// wrap-around preserves.  The accu bound product needs no blocking while q 2^12 < 2^31.  Operand planes are int8 in the tile-contiguous
 // layout of operand_chunk_offset (rows padded to 256, the inner dimension to 256 with
 // zeros), so the kernel needs no bounds checks in the K loop.
 #include "oz2_common.hpp"
@@ -41,6 +46,8 @@ constexpr int kTileBytes = kStageTile;          // 16 KiB per operand per stage
 constexpr int kStageBytes = 2 * kTileBytes;     // A then B
 constexpr int kLoadsPerStage = 8;               // global_load_lds per wave per stage (4 A + 4 B)
 constexpr int kGroupM = 4;  // tile rows per group of the XCD-aware launch order
+constexpr int kKBlock = 1 << 17;                // inner-dimension bytes per launch of the mod GEMM
+static_assert(static_cast<long>(kKBlock) * 127 * 127 < (1L << 31), "odd-modulus block products fit INT32");
 static_assert(kBM == kRowPad && kBN == kRowPad, "operand stage tiles are 256 rows");
 
 // Constants of the output reduction R = P mod m for each modulus (index t).  The
@@ -122,11 +129,13 @@ __device__ __forceinline__ void tile_coords(unsigned wg, int tiles_m, int tiles_
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-enum { kEpiMod = 0, kEpiRawMod = 1, kEpiBound = 2 };
+enum { kEpiMod = 0, kEpiRawMod = 1, kEpiBound = 2, kEpiModAcc = 3 };
 
 template <int EPI>
+// K: padded inner dimension (row length of the operand planes); stages kt0 .. kt0 + nk - 1
+// of it are multiplied.
 __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restrict__ at, const int8_t* __restrict__ bt,
-                                                         long a_plane, long b_plane, int K,
+                                                         long a_plane, long b_plane, int K, int kt0, int nk,
                                                          uint8_t* __restrict__ res, long r_plane, int ldr,
                                                          int32_t* __restrict__ p_dump, int p, int r,
                                                          int* __restrict__ rho, int* __restrict__ gamma,
@@ -142,12 +151,13 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
   tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
   const int i0 = tile_i * kBM;
   const int j0 = tile_j * kBN;
-  const int nk = K / kBK;
 
   // Copies: wave w moves bytes [4096 w + 1024 g, +1024) of each 16 KiB stage tile (g =
   // 0..3 for A, again for B); lane l lands at byte 16 l of that KiB.
-  const int8_t* const ga = at + t * a_plane + static_cast<long>(tile_i) * kBM * K + wave * 4096 + 16 * lane;
-  const int8_t* const gb = bt + t * b_plane + static_cast<long>(tile_j) * kBN * K + wave * 4096 + 16 * lane;
+  const int8_t* const ga = at + t * a_plane + static_cast<long>(tile_i) * kBM * K +
+                           static_cast<long>(kt0) * kTileBytes + wave * 4096 + 16 * lane;
+  const int8_t* const gb = bt + t * b_plane + static_cast<long>(tile_j) * kBN * K +
+                           static_cast<long>(kt0) * kTileBytes + wave * 4096 + 16 * lane;
   auto copy1 = [&](int kbuf, int ksrc, int g) {
     const long src = static_cast<long>(ksrc) * kTileBytes + (g & 3) * 1024;
     int8_t* dst = smem + (kbuf % kStages) * kStageBytes + wave * 4096 + (g & 3) * 1024;
@@ -287,10 +297,18 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int i = ib + mb * 32 + 8 * g;
+          uint32_t* const rp = reinterpret_cast<uint32_t*>(rt + static_cast<long>(j) * ldr + i);
           uint32_t b0 = static_cast<uint32_t>(acc[mb][nb][4 * g]);
           uint32_t b1 = static_cast<uint32_t>(acc[mb][nb][4 * g + 1]);
           uint32_t b2 = static_cast<uint32_t>(acc[mb][nb][4 * g + 2]);
           uint32_t b3 = static_cast<uint32_t>(acc[mb][nb][4 * g + 3]);
+          if constexpr (EPI == kEpiModAcc) {  // (P_block + R_prev) mod m: add the previous residue bytes
+            const uint32_t prev = *rp;
+            b0 += prev & 0xFFu;
+            b1 += (prev >> 8) & 0xFFu;
+            b2 += (prev >> 16) & 0xFFu;
+            b3 += prev >> 24;
+          }
           if (!m256) {  // m = 256: P mod 256 is the low byte of P (h = 0)
             b0 = mod_byte(static_cast<int>(b0), mr);
             b1 = mod_byte(static_cast<int>(b1), mr);
@@ -299,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
           }
           const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
           const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
-          *reinterpret_cast<uint32_t*>(rt + static_cast<long>(j) * ldr + i) = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+          *rp = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
           if constexpr (EPI == kEpiRawMod) {
             if (j < r) {
               int32_t* dst = p_dump + (static_cast<long>(t) * r + j) * p;
@@ -322,25 +340,31 @@ hipError_t launch_gemm(const Work& w, int epi, const DumpPtrs& dump, hipStream_t
   const long a_plane = static_cast<long>(w.p_pad) * w.q_pad;
   const long b_plane = static_cast<long>(w.r_pad) * w.q_pad;
   const long r_plane = static_cast<long>(w.r_pad) * w.p_pad;
-  const int8_t* a = epi == kEpiBound ? w.abar : w.at;
-  const int8_t* b = epi == kEpiBound ? w.bbar : w.bt;
-  switch (epi) {
-    case kEpiMod:
-      hipLaunchKernelGGL(gemm_i8_kernel<kEpiMod>, grid, dim3(256), 0, st, a, b, a_plane, b_plane, w.q_pad, w.res,
-                         r_plane, w.p_pad, nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
-      break;
-    case kEpiRawMod:
-      hipLaunchKernelGGL(gemm_i8_kernel<kEpiRawMod>, grid, dim3(256), 0, st, a, b, a_plane, b_plane, w.q_pad,
-                         w.res, r_plane, w.p_pad, dump.pt, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
-      break;
-    case kEpiBound:
-      hipLaunchKernelGGL(gemm_i8_kernel<kEpiBound>, grid, dim3(256), 0, st, a, b, a_plane, b_plane, w.q_pad,
-                         nullptr, 0L, w.p_pad, nullptr, w.p, w.r, w.rho, w.gamma, tiles_m, tiles_n);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  const int nk = w.q_pad / kBK;
+  if (epi == kEpiBound) {
+    hipLaunchKernelGGL(gemm_i8_kernel<kEpiBound>, grid, dim3(256), 0, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad,
+                       0, nk, nullptr, 0L, w.p_pad, nullptr, w.p, w.r, w.rho, w.gamma, tiles_m, tiles_n);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  if (epi != kEpiMod && epi != kEpiRawMod) return hipErrorInvalidValue;
+  // the raw P_t dump covers one block only (the entry points refuse it for longer q)
+  if (epi == kEpiRawMod && nk > kKBlock / kBK) return hipErrorInvalidValue;
+  constexpr int kBlockStages = kKBlock / kBK;
+  for (int kt0 = 0; kt0 == 0 || kt0 < nk; kt0 += kBlockStages) {
+    const int nkb = nk - kt0 < kBlockStages ? nk - kt0 : kBlockStages;
+    if (kt0 > 0)
+      hipLaunchKernelGGL(gemm_i8_kernel<kEpiModAcc>, grid, dim3(256), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad,
+                         kt0, nkb, w.res, r_plane, w.p_pad, nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
+    else if (epi == kEpiRawMod)
+      hipLaunchKernelGGL(gemm_i8_kernel<kEpiRawMod>, grid, dim3(256), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad,
+                         0, nkb, w.res, r_plane, w.p_pad, dump.pt, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL(gemm_i8_kernel<kEpiMod>, grid, dim3(256), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad,
+                         0, nkb, w.res, r_plane, w.p_pad, nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace oz2

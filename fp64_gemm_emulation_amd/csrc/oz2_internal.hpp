@@ -26,11 +26,21 @@ struct Work {
   int* f_col;               // [r]   accu: max-abs exponents of columns of B
   int* rho;                 // [p]   accu: row maxima of the bound product
   int* gamma;               // [r]   accu: column maxima of the bound product
-  int8_t* at;               // [s][p_pad][q_pad]  A_t (K-permuted in 256-blocks)
-  int8_t* bt;               // [s][r_pad][q_pad]  B_t (same K permutation)
+  int8_t* at;               // s planes of p_pad x q_pad, tile-contiguous (operand_chunk_offset)
+  int8_t* bt;               // s planes of r_pad x q_pad, same layout
   int8_t* abar;             // [p_pad][q_pad]     accu bound inputs (alias of A_t plane 0)
   int8_t* bbar;             // [r_pad][q_pad]     (alias of B_t plane 0)
   uint8_t* res;             // [s][r_pad][p_pad]  R_t, column-major planes
+};
+
+// One FP64 input operand as the kernels see it: its "lines" are the rows of op(A) or the
+// columns of op(B), each q long.  contig: every line is contiguous in memory (columns of
+// a column-major matrix, element k of line n at ptr[n ld + k]); otherwise a line is a
+// row of a column-major matrix (element k of line n at ptr[n + k ld]).
+struct Operand {
+  const double* ptr;
+  long ld;
+  bool contig;
 };
 
 // Optional validation outputs written while the pipeline runs.
@@ -44,24 +54,24 @@ struct DumpPtrs {
 // scaling stage
 hipError_t launch_fill_i32(int* ptr, int value, long n, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st);
-hipError_t launch_fast_scaling(const double* A, long lda, const double* B, long ldb, const Work& w,
-                               hipStream_t st);
-hipError_t launch_accu_bound_inputs(const double* A, long lda, const double* B, long ldb, const Work& w,
-                                    hipStream_t st);
+hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w, hipStream_t st);
+hipError_t launch_accu_bound_inputs(const Operand& a, const Operand& b, const Work& w, hipStream_t st);
 hipError_t launch_accu_exponents(const Work& w, hipStream_t st);
 
 // residue stage
-hipError_t launch_residues(const double* A, long lda, const double* B, long ldb, const Work& w,
-                           const DumpPtrs& dump, hipStream_t st);
+hipError_t launch_residues(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump,
+                           hipStream_t st);
 
 // GEMM stage: epi 0 = R_t only, 1 = R_t and raw P_t dump, 2 = accu bound (rho, gamma)
 hipError_t launch_gemm(const Work& w, int epi, const DumpPtrs& dump, hipStream_t st);
 
 // reconstruction stage
-hipError_t launch_crt(const Work& w, double* C, long ldc, const DumpPtrs& dump, hipStream_t st);
+// C = alpha Chat + beta C (C not read when beta == 0)
+hipError_t launch_crt(const Work& w, double* C, long ldc, double alpha, double beta, const DumpPtrs& dump,
+                      hipStream_t st);
 
-// validation helpers: undo the K permutation / padding of an int8 operand plane set
-// src [planes][rows_pad][q_pad] -> dst [planes][rows][q]
+// validation helper: operand planes in the tile-contiguous layout (padded) -> dst
+// [planes][rows][q], plain row-major
 hipError_t launch_unpermute_i8(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
                                int8_t* dst, hipStream_t st);
 

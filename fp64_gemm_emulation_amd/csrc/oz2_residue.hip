@@ -126,12 +126,15 @@ __device__ __forceinline__ void store_residues(const int (&l)[16][NLHI + 1], int
   }
 }
 
-// Rows of column-major A; thread mapping owner_rows_of_a (the thread's 16 elements of
-// row i are l = 256 blk + L + 16 k).
+// Lines that are rows of a column-major matrix (rows of A, or columns of op(B) = B^T);
+// thread mapping owner_rows_of_a (the thread's 16 elements of line i are
+// l = 256 blk + L + 16 k).  The validation dump of the scaled operand receives element
+// (line, l) at ap_dump[line dls + l dks].
 template <int S, int NLHI, bool DUMP>
 __global__ __launch_bounds__(256) void residues_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
                                                             const int* __restrict__ dsc, int8_t* __restrict__ at,
-                                                            long plane, int q_pad, double* __restrict__ ap_dump) {
+                                                            long plane, int q_pad, double* __restrict__ ap_dump,
+                                                            long dls, long dks) {
   const ChunkOwner own = owner_rows_of_a();
   const int i = own.row;
   const bool row_ok = i < p;
@@ -145,17 +148,19 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(const double* __rest
     double apv;
     scaled_limbs<NLHI>(x, scale, l[k], DUMP ? &apv : nullptr);
     if constexpr (DUMP) {
-      if (ok) ap_dump[i + static_cast<long>(col) * p] = apv;
+      if (ok) ap_dump[i * dls + col * dks] = apv;
     }
   }
   store_residues<S, NLHI, 0>(l, at + operand_chunk_offset(i, own.blk, own.slot, q_pad), plane);
 }
 
-// Columns of column-major B (each column contiguous); thread mapping owner_cols_of_b.
+// Contiguous lines (columns of B, or rows of op(A) = A^T); thread mapping
+// owner_cols_of_b.  Dump as in residues_rows_kernel.
 template <int S, int NLHI, bool DUMP>
 __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                             const int* __restrict__ bsc, int8_t* __restrict__ bt,
-                                                            long plane, int q_pad, double* __restrict__ bp_dump) {
+                                                            long plane, int q_pad, double* __restrict__ bp_dump,
+                                                            long dls, long dks) {
   const ChunkOwner own = owner_cols_of_b();
   const int j = own.row;
   const bool col_ok = j < r;
@@ -170,60 +175,66 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __rest
     double bpv;
     scaled_limbs<NLHI>(x, scale, l[k], DUMP ? &bpv : nullptr);
     if constexpr (DUMP) {
-      if (ok) bp_dump[row + static_cast<long>(j) * q] = bpv;
+      if (ok) bp_dump[j * dls + row * dks] = bpv;
     }
   }
   store_residues<S, NLHI, 0>(l, bt + operand_chunk_offset(j, own.blk, own.slot, q_pad), plane);
 }
 
-template <int S, bool ACCU, bool DUMP>
-static void launch_residues_t(const double* A, long lda, const double* B, long ldb, const Work& w,
-                              const DumpPtrs& dump, hipStream_t st) {
-  constexpr int NL = nl_hi(S, ACCU);
-  const int nblk = w.q_pad / kKPad;
-  if (nblk == 0) return;
-  dim3 grid_a(w.p_pad / 64, w.q_pad / kStageK);
-  hipLaunchKernelGGL((residues_rows_kernel<S, NL, DUMP>), grid_a, dim3(256), 0, st, A, lda, w.p, w.q, w.d, w.at,
-                     static_cast<long>(w.p_pad) * w.q_pad, w.q_pad, dump.ap);
-  dim3 grid_b(w.r_pad / 16, nblk);
-  hipLaunchKernelGGL((residues_cols_kernel<S, NL, DUMP>), grid_b, dim3(256), 0, st, B, ldb, w.q, w.r, w.b, w.bt,
-                     static_cast<long>(w.r_pad) * w.q_pad, w.q_pad, dump.bp);
-}
-
-template <int S>
-static void launch_residues_s(const double* A, long lda, const double* B, long ldb, const Work& w,
-                              const DumpPtrs& dump, hipStream_t st) {
-  const bool d = dump.ap != nullptr || dump.bp != nullptr;
-  if (w.accu) {
-    if (d)
-      launch_residues_t<S, true, true>(A, lda, B, ldb, w, dump, st);
-    else
-      launch_residues_t<S, true, false>(A, lda, B, ldb, w, dump, st);
+// Residue planes of one operand (nlines_pad rows); dump element (line, l) at
+// dump[line dls + l dks].
+template <int S, int NL, bool DUMP>
+static void residues_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, const int* scale,
+                           int8_t* out, double* dump, long dls, long dks, hipStream_t st) {
+  const long plane = static_cast<long>(nlines_pad) * q_pad;
+  if (o.contig) {
+    dim3 grid(nlines_pad / 16, q_pad / kKPad);
+    hipLaunchKernelGGL((residues_cols_kernel<S, NL, DUMP>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, scale,
+                       out, plane, q_pad, dump, dls, dks);
   } else {
-    if (d)
-      launch_residues_t<S, false, true>(A, lda, B, ldb, w, dump, st);
-    else
-      launch_residues_t<S, false, false>(A, lda, B, ldb, w, dump, st);
+    dim3 grid(nlines_pad / 64, q_pad / kStageK);
+    hipLaunchKernelGGL((residues_rows_kernel<S, NL, DUMP>), grid, dim3(256), 0, st, o.ptr, o.ld, nlines, q, scale,
+                       out, plane, q_pad, dump, dls, dks);
   }
 }
 
+template <int S, bool ACCU>
+static void launch_residues_s(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump,
+                              hipStream_t st) {
+  constexpr int NL = nl_hi(S, ACCU);
+  if (w.q_pad == 0) return;
+  // A' dump: column-major p x q (ld p); B' dump: column-major q x r (ld q); each operand
+  // runs the dumping kernel only when its own dump is requested
+  if (dump.ap != nullptr)
+    residues_lines<S, NL, true>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, dump.ap, 1L, static_cast<long>(w.p), st);
+  else
+    residues_lines<S, NL, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, nullptr, 0L, 0L, st);
+  if (dump.bp != nullptr)
+    residues_lines<S, NL, true>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, dump.bp, static_cast<long>(w.q), 1L, st);
+  else
+    residues_lines<S, NL, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, nullptr, 0L, 0L, st);
+}
+
 template <int S>
-static bool dispatch_residues(int s, const double* A, long lda, const double* B, long ldb, const Work& w,
-                              const DumpPtrs& dump, hipStream_t st) {
+static bool dispatch_residues(int s, const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump,
+                              hipStream_t st) {
   if constexpr (S > kMaxS) {
     return false;
   } else {
     if (s == S) {
-      launch_residues_s<S>(A, lda, B, ldb, w, dump, st);
+      if (w.accu)
+        launch_residues_s<S, true>(a, b, w, dump, st);
+      else
+        launch_residues_s<S, false>(a, b, w, dump, st);
       return true;
     }
-    return dispatch_residues<S + 1>(s, A, lda, B, ldb, w, dump, st);
+    return dispatch_residues<S + 1>(s, a, b, w, dump, st);
   }
 }
 
-hipError_t launch_residues(const double* A, long lda, const double* B, long ldb, const Work& w,
-                           const DumpPtrs& dump, hipStream_t st) {
-  if (!dispatch_residues<kMinS>(w.s, A, lda, B, ldb, w, dump, st)) return hipErrorInvalidValue;
+hipError_t launch_residues(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump,
+                           hipStream_t st) {
+  if (!dispatch_residues<kMinS>(w.s, a, b, w, dump, st)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

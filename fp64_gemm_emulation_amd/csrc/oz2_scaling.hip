@@ -30,9 +30,10 @@ __global__ void fill_u32_kernel(unsigned* __restrict__ p, unsigned v, long n) {
   if (i < n) p[i] = v;
 }
 
-// Rows of column-major A: 64 rows (one per lane) x one kChunk block per workgroup;
-// wave w reads l in [c kChunk + 64 w, +64).  Each load instruction reads 64 consecutive
-// rows of one column.  MAXONLY: only the block max-abs exponents are produced.
+// Lines that are rows of a column-major matrix (rows of A, or columns of op(B) = B^T):
+// 64 lines (one per lane) x one kChunk block per workgroup; wave w reads l in
+// [c kChunk + 64 w, +64).  Each load instruction reads 64 consecutive rows of one
+// column.  MAXONLY: only the block max-abs exponents are produced.
 template <bool MAXONLY>
 __global__ __launch_bounds__(256) void stats_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
                                                          int nch, int* __restrict__ part_e,
@@ -86,8 +87,9 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const double* __restric
   }
 }
 
-// Columns of column-major B (contiguous): one wave per (column j, block c); lane reads
-// l = c kChunk + lane + 64 k, k = 0..3, so every load instruction is 512 contiguous bytes.
+// Contiguous lines (columns of B, or rows of op(A) = A^T): one wave per (line j, block c);
+// lane reads l = c kChunk + lane + 64 k, k = 0..3, so every load instruction is 512
+// contiguous bytes.
 template <bool MAXONLY>
 __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                          int nch, int* __restrict__ part_e,
@@ -176,9 +178,10 @@ __global__ void max_exponents_kernel(int na, int nb, int nch, const int* __restr
     f_col[line] = e;
 }
 
-// accu bound inputs of the rows of A: Abar_il = ceil(|a_il| 2^(kQBits - e_i)) in [0, 64],
-// written in the tile-contiguous operand layout (zeros in the padding); thread mapping
-// owner_rows_of_a, the thread covers l = 256 blk + L + 16 k.
+// accu bound inputs of lines that are rows of a column-major matrix:
+// Abar_il = ceil(|a_il| 2^(kQBits - e_i)) in [0, 64], written in the tile-contiguous
+// operand layout (zeros in the padding); thread mapping owner_rows_of_a, the thread
+// covers l = 256 blk + L + 16 k.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
                                                          int q_pad, const int* __restrict__ e_row,
                                                          int8_t* __restrict__ abar) {
@@ -201,8 +204,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const double* __restric
   *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
-// accu bound inputs of the columns of B (each column contiguous); thread mapping
-// owner_cols_of_b.
+// accu bound inputs of contiguous lines; thread mapping owner_cols_of_b.
 __global__ __launch_bounds__(256) void quant_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                          int q_pad, const int* __restrict__ f_col,
                                                          int8_t* __restrict__ bbar) {
@@ -262,25 +264,29 @@ hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st
   return hipGetLastError();
 }
 
+// Block statistics of the lines of one operand (rows of op(A) or columns of op(B)).
 template <bool MAXONLY>
-static hipError_t launch_stats(const double* A, long lda, const double* B, long ldb, const Work& w,
-                               hipStream_t st) {
-  if (w.nch > 0 && w.p > 0) {
-    dim3 grid(blocks_for(w.p, kWave), w.nch);
-    hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(256), 0, st, A, lda, w.p, w.q, w.nch, w.part_e_a,
-                       w.part_s_a, w.flags);
+static void stats_lines(const Operand& o, int nlines, int q, int nch, int* pe, double* ps, unsigned* flags,
+                        hipStream_t st) {
+  if (nch == 0 || nlines == 0) return;
+  if (o.contig) {
+    dim3 grid(nlines, blocks_for(nch, 4));
+    hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps, flags);
+  } else {
+    dim3 grid(blocks_for(nlines, kWave), nch);
+    hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, nlines, q, nch, pe, ps, flags);
   }
-  if (w.nch > 0 && w.r > 0) {
-    dim3 grid(w.r, blocks_for(w.nch, 4));
-    hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, B, ldb, w.q, w.r, w.nch, w.part_e_b,
-                       w.part_s_b, w.flags);
-  }
+}
+
+template <bool MAXONLY>
+static hipError_t launch_stats(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
+  stats_lines<MAXONLY>(a, w.p, w.q, w.nch, w.part_e_a, w.part_s_a, w.flags, st);
+  stats_lines<MAXONLY>(b, w.r, w.q, w.nch, w.part_e_b, w.part_s_b, w.flags, st);
   return hipGetLastError();
 }
 
-hipError_t launch_fast_scaling(const double* A, long lda, const double* B, long ldb, const Work& w,
-                               hipStream_t st) {
-  hipError_t e = launch_stats<false>(A, lda, B, ldb, w, st);
+hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
+  hipError_t e = launch_stats<false>(a, b, w, st);
   if (e != hipSuccess) return e;
   const int n = w.p + w.r;
   hipLaunchKernelGGL(fast_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.nch,
@@ -288,20 +294,27 @@ hipError_t launch_fast_scaling(const double* A, long lda, const double* B, long 
   return hipGetLastError();
 }
 
-hipError_t launch_accu_bound_inputs(const double* A, long lda, const double* B, long ldb, const Work& w,
-                                    hipStream_t st) {
-  hipError_t e = launch_stats<true>(A, lda, B, ldb, w, st);
+// accu quantized operand plane of one operand (nlines_pad rows, tile-contiguous layout)
+static void quant_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, const int* e, int8_t* out,
+                        hipStream_t st) {
+  if (q_pad == 0) return;
+  if (o.contig) {
+    dim3 grid(nlines_pad / 16, q_pad / kKPad);
+    hipLaunchKernelGGL(quant_cols_kernel, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, q_pad, e, out);
+  } else {
+    dim3 grid(nlines_pad / 64, q_pad / kStageK);
+    hipLaunchKernelGGL(quant_rows_kernel, grid, dim3(256), 0, st, o.ptr, o.ld, nlines, q, q_pad, e, out);
+  }
+}
+
+hipError_t launch_accu_bound_inputs(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
+  hipError_t e = launch_stats<true>(a, b, w, st);
   if (e != hipSuccess) return e;
   const int n = w.p + w.r;
   hipLaunchKernelGGL(max_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.nch,
                      w.part_e_a, w.part_e_b, w.e_row, w.f_col);
-  const int nblk = w.q_pad / kKPad;
-  if (nblk > 0) {
-    dim3 grid_a(w.p_pad / 64, w.q_pad / kStageK);
-    hipLaunchKernelGGL(quant_rows_kernel, grid_a, dim3(256), 0, st, A, lda, w.p, w.q, w.q_pad, w.e_row, w.abar);
-    dim3 grid_b(w.r_pad / 16, nblk);
-    hipLaunchKernelGGL(quant_cols_kernel, grid_b, dim3(256), 0, st, B, ldb, w.q, w.r, w.q_pad, w.f_col, w.bbar);
-  }
+  quant_lines(a, w.p, w.p_pad, w.q, w.q_pad, w.e_row, w.abar, st);
+  quant_lines(b, w.r, w.r_pad, w.q, w.q_pad, w.f_col, w.bbar, st);
   // the bound GEMM accumulates maxima with atomics: start from 0
   if ((e = launch_fill_i32(w.rho, 0, w.p, st)) != hipSuccess) return e;
   if ((e = launch_fill_i32(w.gamma, 0, w.r, st)) != hipSuccess) return e;

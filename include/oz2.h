@@ -11,6 +11,7 @@
  *   A' = trunc(D A),  B' = trunc(B E)
  *   A_t = rho_{m_t}(A'),  B_t = rho_{m_t}(B')      centered int8 residues, t = 1..s
  *   P_t = A_t B_t                                  int8 x int8 -> int32, exact for q < 2^17
+ *                                                  (longer q: blocked, each block reduced mod m_t)
  *   R_t = P_t mod m_t                              nonnegative, uint8
  *   X   = CRT(R_1..R_s) in [-M/2, M/2),  M = prod m_t
  *   C   = D^-1 X E^-1
@@ -20,7 +21,8 @@
  *
  * Conventions for every entry point:
  *   - Matrices are column-major FP64: A is p x q with leading dimension lda >= max(1,p),
- *     B is q x r with ldb >= max(1,q), C is p x r with ldc >= max(1,p).
+ *     B is q x r with ldb >= max(1,q), C is p x r with ldc >= max(1,p) (ozaki2_dgemm_ex
+ *     also takes transposed A and B).
  *   - Matrix and workspace pointers are DEVICE pointers on the current HIP device.
  *     C must not overlap A, B or the workspace.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
@@ -50,15 +52,22 @@ typedef enum {
 enum {
   OZ2_OK = 0,
   OZ2_ERR_ARG = 1,         /* invalid size, leading dimension, pointer, s or mode */
-  OZ2_ERR_UNSUPPORTED = 2, /* q >= 2^17: INT32 accumulation no longer provably exact */
+  OZ2_ERR_UNSUPPORTED = 2, /* q > OZ2_MAX_Q, a size whose launch grid would not fit, or a raw P_t
+                              dump requested with q > OZ2_MAX_Q_P_DUMP */
   OZ2_ERR_WORKSPACE = 3,   /* caller workspace too small, or device allocation failed */
   OZ2_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 };
 
 #define OZ2_MIN_S 2
 #define OZ2_MAX_S 20
-/* Largest inner dimension: q * 128^2 < 2^31 iff q < 2^17 ("Ozaki II supplement", section 1.3). */
-#define OZ2_MAX_Q 131071
+/* One INT32 dot product of int8 residues is exact while q 128^2 < 2^31, i.e. q < 2^17
+ * ("Ozaki II supplement", section 1.3).  Longer inner dimensions are split into blocks of
+ * 65536 whose partial products are reduced mod m_t before they are combined, which is
+ * exact for any q; the limit below comes from the accu bound product, whose INT32 entries
+ * are at most q 64^2. */
+#define OZ2_MAX_Q 524287
+/* Largest q for which the raw P_t dump of ozaki2_dgemm_debug is defined (exact INT32). */
+#define OZ2_MAX_Q_P_DUMP 131071
 /* X is dumped as a 160-bit two's-complement integer in 5 little-endian 32-bit limbs. */
 #define OZ2_X_LIMBS 5
 
@@ -76,6 +85,27 @@ enum {
  */
 int ozaki2_dgemm(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
                  double* C, int ldc, int s, int mode, void* stream);
+
+/* Operation applied to an input matrix by ozaki2_dgemm_ex. */
+typedef enum {
+  OZ2_OP_N = 0, /* the matrix as stored */
+  OZ2_OP_T = 1  /* its transpose */
+} oz2_op_t;
+
+/*
+ * ozaki2_dgemm_ex -- C = alpha op(A) op(B) + beta C, the product emulated as in
+ * ozaki2_dgemm with op(A) (p x q) and op(B) (q x r) in place of A and B.
+ *   transa : OZ2_OP_N: A is p x q, lda >= max(1,p);  OZ2_OP_T: A is q x p, lda >= max(1,q).
+ *   transb : OZ2_OP_N: B is q x r, ldb >= max(1,q);  OZ2_OP_T: B is r x q, ldb >= max(1,r).
+ *   C      : p x r, ldc >= max(1,p).  With Chat the emulated product (the value ozaki2_dgemm
+ *            stores), each entry becomes alpha * Chat when beta == 0 (C is then not read,
+ *            so it may hold anything) and fma(alpha, Chat, beta * C) otherwise.
+ * alpha = 1, beta = 0 with OZ2_OP_N twice is exactly ozaki2_dgemm.  The scalings are those
+ * of op(A) and op(B): rows of op(A) and columns of op(B).  Same workspace, errors and
+ * ordering rules as ozaki2_dgemm; transa/transb outside oz2_op_t give OZ2_ERR_ARG.
+ */
+int ozaki2_dgemm_ex(int transa, int transb, int p, int q, int r, double alpha, const double* A, int lda,
+                    const double* B, int ldb, double beta, double* C, int ldc, int s, int mode, void* stream);
 
 /* Bytes of device workspace ozaki2_dgemm / ozaki2_dgemm_debug need for these sizes
  * (0 if the arguments are invalid or describe no work). */
@@ -97,7 +127,7 @@ int ozaki2_release(void);
  *   Bp[q*r]              B' as exact FP64 integers, column-major, ld q
  *   At[s*p*q]            A_t[i][l] at At[(t*p + i)*q + l]
  *   Bt[s*r*q]            B_t[l][j] at Bt[(t*r + j)*q + l]
- *   P[s*r*p]             P_t[i][j] at P[(t*r + j)*p + i]   (int32)
+ *   P[s*r*p]             P_t[i][j] at P[(t*r + j)*p + i]   (int32; only for q <= OZ2_MAX_Q_P_DUMP)
  *   R[s*r*p]             R_t[i][j] at R[(t*r + j)*p + i]   (uint8)
  *   X[r*p*5]             X[i][j] at X[(j*p + i)*5 + k], k = 0..4 little-endian limbs
  * accu mode only (ignored in fast mode):

@@ -20,7 +20,8 @@ Pipeline ([P] Part I section 1, stage table; [S] section 1.1):
 Everything here is exact: integers are NumPy int64 where they provably fit and
 Python ints otherwise; the only library primitive is a float64 matrix product
 for P_t, which is exact because every term is an integer of magnitude <= 2^14
-and every partial sum stays below q * 2^14 < 2^31 < 2^53 ([S] section 1.3).
+and every partial sum stays below q * 2^14 < 2^53 (below 2^31 for q < 2^17,
+[S] section 1.3; the oracle takes any q).
 
 Readings taken where the pages leave a step open (each also listed in the
 design notes of the repository):
@@ -472,6 +473,29 @@ def ozaki2_sample(A, B, s: int, mode: str, rows, cols) -> dict:
     out.update(d=d, b=b, Ap=ap, Bp=bp, At=at, Bt=bt, P=pt, R=rt, X=x, C=c, moduli=mods,
                rows=rows, cols=cols)
     return out
+
+
+def alpha_beta_update(c_hat: np.ndarray, alpha: float, beta: float, c: np.ndarray | None = None) -> np.ndarray:
+    """C <- alpha C_hat + beta C, the update of the library's general entry point.
+
+    The pages define only C = A B; scaling the product and accumulating into C follow
+    the usual GEMM convention, with this rounding: beta == 0 gives RN(alpha C_hat) and
+    C is not read; otherwise RN(alpha C_hat + RN(beta C)), one rounding of the sum (a
+    fused multiply-add).  Computed with exact rationals and one correctly rounded
+    conversion per entry.
+    """
+    c_hat = np.asarray(c_hat, dtype=np.float64)
+    out = np.empty_like(c_hat)
+    fa = Fraction(alpha)
+    for idx in np.ndindex(c_hat.shape):
+        v = fa * Fraction(float(c_hat[idx]))
+        if beta != 0.0:
+            v += Fraction(float(np.float64(beta) * np.float64(c[idx])))
+        out[idx] = float(v)
+    return out
+
+
+__all__.append("alpha_beta_update")
 
 
 def exact_product(A: np.ndarray, B: np.ndarray):

@@ -73,18 +73,47 @@ def test_argument_validation_before_launch(lib):
     assert run(ldc=7) == lib.OZ2_ERR_ARG
     assert run(C=None) == lib.OZ2_ERR_ARG
     assert run(A=None) == lib.OZ2_ERR_ARG
-    assert run(q=131072, ldb=131072) == lib.OZ2_ERR_UNSUPPORTED
+    assert run(q=524288, ldb=524288) == lib.OZ2_ERR_UNSUPPORTED   # beyond OZ2_MAX_Q
     assert run(C=A + 8) == lib.OZ2_ERR_ARG          # C overlaps A
     assert run(p=0) == lib.OZ2_OK                     # empty: no work, nothing launched
     assert run(r=0) == lib.OZ2_OK
     assert lib.ozaki2_dgemm_debug(8, 8, 8, A, 8, B, 8, C, 8, 1, 0, None, None) == lib.OZ2_ERR_ARG
+    # the raw P_t dump is exact int32 only without K-blocking
+    dump = lib.OZ2Dump(P=0x60000000)
+    q = lib.OZ2_MAX_Q_P_DUMP + 1
+    assert lib.ozaki2_dgemm_debug(8, q, 8, A, 8, B, q, C, 8, 8, 0, None, dump) == lib.OZ2_ERR_UNSUPPORTED
+
+
+def test_ex_argument_validation_before_launch(lib):
+    """ozaki2_dgemm_ex: operation codes and the leading dimensions of transposed operands."""
+    A, B, C = 0x10000, 0x20000000, 0x40000000  # never dereferenced
+    N, T = lib.OZ2_OP_N, lib.OZ2_OP_T
+    ok = dict(ta=N, tb=N, p=8, q=6, r=4, alpha=1.0, A=A, lda=8, B=B, ldb=6, beta=0.0, C=C, ldc=8, s=8, mode=0)
+
+    def run(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.ozaki2_dgemm_ex(a["ta"], a["tb"], a["p"], a["q"], a["r"], a["alpha"], a["A"], a["lda"], a["B"],
+                                   a["ldb"], a["beta"], a["C"], a["ldc"], a["s"], a["mode"], None)
+
+    assert run(ta=2) == lib.OZ2_ERR_ARG
+    assert run(tb=-1) == lib.OZ2_ERR_ARG
+    assert run(lda=7) == lib.OZ2_ERR_ARG                 # A is p x q: lda >= p
+    assert run(ta=T, lda=5) == lib.OZ2_ERR_ARG           # A is q x p: lda >= q
+    assert run(ldb=5) == lib.OZ2_ERR_ARG                 # B is q x r: ldb >= q
+    assert run(tb=T, ldb=3) == lib.OZ2_ERR_ARG           # B is r x q: ldb >= r
+    assert run(C=A + 8) == lib.OZ2_ERR_ARG               # C overlaps A
+    assert run(ta=T, C=A + 8 * 6 * 7) == lib.OZ2_ERR_ARG  # last element of the q x p A
+    assert run(p=0) == lib.OZ2_OK
+    assert run(s=21) == lib.OZ2_ERR_ARG
 
 
 def test_workspace_size(lib):
     ws = lib.ozaki2_workspace_size
     assert ws(0, 8, 8, 8, 0) == 0
     assert ws(8, 8, 8, 1, 0) == 0
-    assert ws(8, 131072, 8, 8, 0) == 0
+    assert ws(8, 524288, 8, 8, 0) == 0
+    assert ws(8, 131072, 8, 8, 0) > 0                  # K-blocked inner dimensions
     small = ws(100, 100, 100, 8, 0)
     assert small > 0 and small % 256 == 0
     assert ws(100, 100, 100, 14, 0) > small

@@ -1,0 +1,114 @@
+"""GPU parity of the general entry point ozaki2_dgemm_ex and of K-blocked inner dimensions.
+
+* transposed operands: ozaki2_dgemm_ex on A^T / B^T as stored must give exactly the
+  result of ozaki2_dgemm on explicit copies of op(A), op(B) (same scalings, residues and
+  CRT), and that result must match the oracle on op(A), op(B);
+* alpha / beta: C <- alpha C_hat + beta C as oracle.alpha_beta_update defines it;
+* q beyond 2^17: the GEMM folds its accumulators mod m every 65536 inner-dimension
+  bytes; d, b, R_t and X must stay bit-exact against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp64_gemm_emulation_amd.workloads import generate
+from tests.gpu_helpers import assert_chat_close, assert_equal, chat_tolerance, log, to_device, x_limbs_to_int
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def oz():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    from fp64_gemm_emulation_amd import binding
+    return binding
+
+
+def _padded(a_np, extra):
+    """Column-major device copy of a_np with leading dimension rows + extra."""
+    import torch
+    rows, cols = a_np.shape
+    buf = torch.full((cols, rows + extra), float("nan"), dtype=torch.float64, device="cuda")
+    buf[:, :rows] = torch.from_numpy(np.ascontiguousarray(a_np.T)).cuda()
+    return buf.t()[:rows, :]
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True), (True, True)])
+def test_transposed_operands(oz, mode, ta, tb):
+    p, q, r, s = 300, 517, 129, 14
+    opA = generate(p, q, 1.0, 41)
+    opB = generate(q, r, 1.0, 42)
+    log(f"[ex] transa={ta} transb={tb} mode={mode} p,q,r={p},{q},{r}")
+    A_stored = _padded(opA.T if ta else opA, 3)
+    B_stored = _padded(opB.T if tb else opB, 5)
+    c_ex = oz.dgemm_ex(A_stored, B_stored, transa=ta, transb=tb, s=s, mode=mode).cpu().numpy()
+    c_plain = oz.dgemm(to_device(opA), to_device(opB), s, mode).cpu().numpy()
+    assert_equal(c_ex, c_plain, "ozaki2_dgemm_ex vs ozaki2_dgemm on op(A), op(B)")
+    ref = oracle.ozaki2(opA, opB, s, mode)
+    assert_chat_close(c_ex, ref["C"], chat_tolerance(opA, opB, np.arange(p), np.arange(r)), "C")
+    log(f"[ex] ok ({int(np.sum(c_ex != ref['C']))} entries differ from the correctly rounded value)")
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+@pytest.mark.parametrize("alpha,beta", [(-0.75, 1.5), (2.0, 0.0), (1.0, -1.0), (0.0, 0.5)])
+def test_alpha_beta(oz, mode, alpha, beta):
+    import torch
+    p, q, r, s = 130, 260, 70, 14
+    A = generate(p, q, 0.5, 51)
+    B = generate(q, r, 0.5, 52)
+    C0 = generate(p, r, 0.5, 53) if beta != 0.0 else np.full((p, r), np.nan)
+    log(f"[ex] alpha={alpha} beta={beta} mode={mode}")
+    Cd = to_device(C0)
+    got = oz.dgemm_ex(to_device(A), to_device(B), alpha=alpha, beta=beta, C=Cd, s=s, mode=mode).cpu().numpy()
+    ref = oracle.ozaki2(A, B, s, mode)
+    want = oracle.alpha_beta_update(ref["C"], alpha, beta, C0)
+    tol = abs(alpha) * chat_tolerance(A, B, np.arange(p), np.arange(r)) + 2.0 ** -52 * np.abs(want)
+    assert_chat_close(got, want, tol, "alpha C_hat + beta C")
+    assert torch.isfinite(torch.from_numpy(got)).all()
+    log(f"[ex] ok ({int(np.sum(got != want))} entries differ from the oracle's update)")
+
+
+def test_empty_inner_dimension_scales_c(oz):
+    p, r = 33, 17
+    C0 = generate(p, r, 0.5, 61)
+    Cd = to_device(C0)
+    import torch
+    A = torch.empty((p, 0), dtype=torch.float64, device="cuda")
+    B = torch.empty((0, r), dtype=torch.float64, device="cuda")
+    got = oz.dgemm_ex(A, B, alpha=3.0, beta=-2.0, C=Cd, s=8).cpu().numpy()
+    assert_equal(got, oracle.alpha_beta_update(np.zeros((p, r)), 3.0, -2.0, C0), "q = 0")
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_k_blocked_inner_dimension(oz, mode):
+    """q = 131372: the GEMM folds its accumulators at stages 1023 and 2047."""
+    p, q, r, s = 40, 131372, 24, 8
+    A = generate(p, q, 0.5, 71)
+    B = generate(q, r, 0.5, 72)
+    log(f"[kblock] mode={mode} p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=("d", "b", "R", "X"))
+    ref = oracle.ozaki2(A, B, s, mode)
+    assert_equal(out["d"].cpu().numpy(), ref["d"].astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), ref["b"].astype(np.int32), "b")
+    rt = out["R"].cpu().numpy()
+    for t in range(s):
+        assert_equal(rt[t], ref["R"][t].T.astype(np.uint8), f"R_t t={t}")
+    xg = out["X"].cpu().numpy()
+    for j in range(r):
+        for i in range(p):
+            assert x_limbs_to_int(xg[j, i]) == int(ref["X"][i, j]), f"X[{i},{j}]"
+    assert_chat_close(out["C"].cpu().numpy(), ref["C"], chat_tolerance(A, B, np.arange(p), np.arange(r)), "C")
+    log("[kblock] ok")
+
+
+def test_p_dump_refused_when_k_blocked(oz):
+    import torch
+    p, q, r = 8, oz.OZ2_MAX_Q_P_DUMP + 1, 8
+    A = torch.zeros((p, q), dtype=torch.float64, device="cuda").t().contiguous().t()
+    B = torch.zeros((q, r), dtype=torch.float64, device="cuda").t().contiguous().t()
+    with pytest.raises(oz.Oz2Error) as info:
+        oz.dgemm_debug(A, B, 8, "fast", want=("P",))
+    assert info.value.status == oz.OZ2_ERR_UNSUPPORTED

@@ -374,3 +374,24 @@ def test_sampled_entries_equal_full_run(mode):
     assert np.array_equal(smp["b"], full["b"][cols])
     assert np.array_equal(smp["C"], full["C"][np.ix_(rows, cols)])
     assert all(int(a) == int(b) for a, b in zip(smp["X"].ravel(), full["X"][np.ix_(rows, cols)].ravel()))
+
+
+def test_alpha_beta_update_pins():
+    """The general entry point's update C <- alpha C_hat + beta C, pinned to facts outside
+    the oracle: numpy's correctly rounded multiply, exact small-integer arithmetic, and a
+    fused multiply-add case whose single rounding differs from two roundings."""
+    rng = np.random.default_rng(11)
+    c_hat = rng.standard_normal((5, 7))
+    c = rng.standard_normal((5, 7))
+    assert np.array_equal(oracle.alpha_beta_update(c_hat, 1.0, 0.0), c_hat)
+    assert np.array_equal(oracle.alpha_beta_update(c_hat, 0.3, 0.0, c), 0.3 * c_hat)
+    # beta == 0 never reads C
+    assert np.array_equal(oracle.alpha_beta_update(c_hat, 2.0, 0.0, np.full_like(c, np.nan)), 2.0 * c_hat)
+    ch = rng.integers(-1000, 1000, (4, 4)).astype(np.float64)
+    ci = rng.integers(-1000, 1000, (4, 4)).astype(np.float64)
+    assert np.array_equal(oracle.alpha_beta_update(ch, 3.0, -2.0, ci), 3.0 * ch - 2.0 * ci)
+    a = 1.0 + 2.0 ** -30
+    two_roundings = a * a - 1.0          # RN(a a) drops the 2^-60 term
+    assert two_roundings == 2.0 ** -29
+    got = oracle.alpha_beta_update(np.array([[a]]), a, 1.0, np.array([[-1.0]]))
+    assert got[0, 0] == 2.0 ** -29 + 2.0 ** -60
