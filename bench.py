@@ -72,6 +72,7 @@ def cpu_baseline(A, B, s, mode, rows, cols):
         blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas_threads = 1
+    rows, cols = min(rows, A.shape[0]), min(cols, B.shape[1])
     t0 = time.perf_counter()
     oracle.ozaki2_sample(A, B, s, mode, np.arange(rows), np.arange(cols))
     dt = time.perf_counter() - t0
@@ -129,6 +130,95 @@ def mfma_ceiling(blocks=1024, rounds=3584, reps=5):
     return ops / (ms * 1e-3) / 1e12
 
 
+def exact_dot_samples(A, B, rows, cols):
+    """Exact (A B)_ij for the sampled entries, as Fractions (integer arithmetic on the FP64
+    significands; independent of the library and of the test oracle)."""
+    import numpy as np
+    from fractions import Fraction
+
+    def ints(v):
+        m, e = np.frexp(v)
+        return [int(x) for x in (m * 2.0 ** 53).astype(np.int64)], (e.astype(np.int64) - 53).tolist()
+
+    out = {}
+    for i in rows:
+        ma, ea = ints(A[i, :])
+        for j in cols:
+            mb, eb = ints(B[:, j])
+            ex = [x + y for x, y in zip(ea, eb)]
+            e0 = min(ex)
+            total = sum((x * y) << (e - e0) for x, y, e in zip(ma, mb, ex))
+            out[(i, j)] = Fraction(total) * Fraction(2) ** e0 if e0 >= 0 else Fraction(total, 2 ** (-e0))
+    return out
+
+
+def rel_errors(C_sample, exact, absab):
+    """|C_ij - (AB)_ij| / (|A||B|)_ij over the samples."""
+    from fractions import Fraction
+    errs = []
+    for (i, j), v in exact.items():
+        errs.append(float(abs(Fraction(float(C_sample[(i, j)])) - v) / Fraction(float(absab[(i, j)]))))
+    return errs
+
+
+def sweep(args):
+    """s- and n-sweep of the emulated product (fast and accu): time per call, stage
+    breakdown and error against the exact product on sampled entries; one JSON line per
+    configuration.  Inputs: the phi = 0.5 generator of the headline workload."""
+    import numpy as np
+    import torch
+
+    from fp64_gemm_emulation_amd import binding
+    from fp64_gemm_emulation_amd.workloads import generate
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(99)
+    for n in args.sweep_n:
+        A = generate(n, n, args.sweep_phi, 1)
+        B = generate(n, n, args.sweep_phi, 2)
+        rows = sorted(rng.choice(n, size=8, replace=False).tolist())
+        cols = sorted(rng.choice(n, size=8, replace=False).tolist())
+        exact = exact_dot_samples(A, B, rows, cols)
+        absab = {(i, j): float(np.abs(A[i, :]) @ np.abs(B[:, j])) for i in rows for j in cols}
+        Ad = binding.colmajor(torch.from_numpy(np.ascontiguousarray(A)).to(dev))
+        Bd = binding.colmajor(torch.from_numpy(np.ascontiguousarray(B)).to(dev))
+        C = binding.empty_colmajor(n, n, device=dev)
+        ri = torch.tensor(rows, device=dev)
+        ci = torch.tensor(cols, device=dev)
+
+        def samples(M):  # the sampled entries only: no full device-to-host copy
+            sub = M[ri][:, ci].cpu().numpy()
+            return {(i, j): sub[a, b] for a, i in enumerate(rows) for b, j in enumerate(cols)}
+
+        nerr = rel_errors(samples(torch.matmul(Ad, Bd)), exact, absab)
+        print(json.dumps({"sweep": "native_fp64", "n": n, "max_rel_err": max(nerr)}), flush=True)
+        for mode in args.sweep_modes:
+            for s in args.sweep_s:
+                for _ in range(2):
+                    binding.dgemm(Ad, Bd, s, mode, out=C, stream=stream)
+                torch.cuda.synchronize()
+                steps = args.sweep_steps
+                assert binding.ozaki2_timing_begin(steps) == binding.OZ2_OK
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    binding.dgemm(Ad, Bd, s, mode, out=C, stream=stream)
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) * 1e3 / steps
+                rc, stage_ms, ncalls = binding.ozaki2_timing_end()
+                st = [v / ncalls for v in stage_ms]
+                errs = rel_errors(samples(C), exact, absab)
+                print(json.dumps({"sweep": "ozaki2", "n": n, "mode": mode, "s": s, "ms_per_call": ms,
+                                  "eff_tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12,
+                                  "stage_ms": {"scaling": st[0], "residues": st[1], "gemm": st[2], "crt": st[3]},
+                                  "gemm_int8_tops": s * 2.0 * n ** 3 / (st[2] * 1e-3) / 1e12,
+                                  "max_rel_err": max(errs), "median_rel_err": sorted(errs)[len(errs) // 2]}),
+                      flush=True)
+        del Ad, Bd, C
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,16 +228,27 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context figures (native FP64 matmul, MFMA ceiling on random operands)")
-    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--cpu-rows", type=int, default=192)
     ap.add_argument("--cpu-cols", type=int, default=2048)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="s- and n-sweep (one JSON line per configuration) instead of the benchmark line")
+    ap.add_argument("--sweep-n", type=int, nargs="+", default=[1024, 2048, 4096, 8192])
+    ap.add_argument("--sweep-s", type=int, nargs="+", default=list(range(2, 21)))
+    ap.add_argument("--sweep-modes", nargs="+", default=["fast", "accu"])
+    ap.add_argument("--sweep-phi", type=float, default=0.5)
+    ap.add_argument("--sweep-steps", type=int, default=5)
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the emulated GEMM is "
               f"measured on one MI355X only", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args)
+        return
 
     import numpy as np
     import torch
