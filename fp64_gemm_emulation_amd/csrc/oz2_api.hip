@@ -255,8 +255,8 @@ int run(const Call& c, void* stream, const oz2_dump_t* dump) {
     OZ2_TRY(oz2::launch_fast_scaling(opa, opb, w, st));
   } else {
     OZ2_TRY(oz2::launch_accu_bound_inputs(opa, opb, w, st));
-    if (dz.Abar != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.abar, 1, p, w.p_pad, q, w.q_pad, dz.Abar, st));
-    if (dz.Bbar != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.bbar, 1, r, w.r_pad, q, w.q_pad, dz.Bbar, st));
+    if (dz.Abar != nullptr) OZ2_TRY(oz2::launch_unpack_operands(w.abar, 1, p, w.p_pad, q, w.q_pad, dz.Abar, st));
+    if (dz.Bbar != nullptr) OZ2_TRY(oz2::launch_unpack_operands(w.bbar, 1, r, w.r_pad, q, w.q_pad, dz.Bbar, st));
     OZ2_TRY(oz2::launch_gemm(w, 2, dp, st));
     OZ2_TRY(oz2::launch_accu_exponents(w, st));
     if (dz.e != nullptr) OZ2_TRY(hipMemcpyAsync(dz.e, w.e_row, sizeof(int) * p, hipMemcpyDeviceToDevice, st));
@@ -270,8 +270,8 @@ int run(const Call& c, void* stream, const oz2_dump_t* dump) {
   OZ2_TRY(rec.mark(1));
   // --- residues ---
   OZ2_TRY(oz2::launch_residues(opa, opb, w, dp, st));
-  if (dz.At != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.at, s, p, w.p_pad, q, w.q_pad, dz.At, st));
-  if (dz.Bt != nullptr) OZ2_TRY(oz2::launch_unpermute_i8(w.bt, s, r, w.r_pad, q, w.q_pad, dz.Bt, st));
+  if (dz.At != nullptr) OZ2_TRY(oz2::launch_unpack_operands(w.at, s, p, w.p_pad, q, w.q_pad, dz.At, st));
+  if (dz.Bt != nullptr) OZ2_TRY(oz2::launch_unpack_operands(w.bt, s, r, w.r_pad, q, w.q_pad, dz.Bt, st));
   OZ2_TRY(rec.mark(2));
   // --- GEMMs + output reduction ---
   OZ2_TRY(oz2::launch_gemm(w, dz.P != nullptr ? 1 : 0, dp, st));
@@ -407,7 +407,7 @@ const char* ozaki2_status_string(int status) {
     case OZ2_ERR_ARG:
       return "invalid argument";
     case OZ2_ERR_UNSUPPORTED:
-      return "unsupported: inner dimension q must be below 2^17";
+      return "unsupported: q above OZ2_MAX_Q, a launch grid beyond its limits, or a P_t dump with q above OZ2_MAX_Q_P_DUMP";
     case OZ2_ERR_WORKSPACE:
       return "workspace too small or device allocation failed";
     case OZ2_ERR_HIP:

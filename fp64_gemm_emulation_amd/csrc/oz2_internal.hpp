@@ -72,7 +72,7 @@ hipError_t launch_crt(const Work& w, double* C, long ldc, double alpha, double b
 
 // validation helper: operand planes in the tile-contiguous layout (padded) -> dst
 // [planes][rows][q], plain row-major
-hipError_t launch_unpermute_i8(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
+hipError_t launch_unpack_operands(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
                                int8_t* dst, hipStream_t st);
 
 }  // namespace oz2

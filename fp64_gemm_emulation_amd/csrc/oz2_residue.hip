@@ -242,7 +242,7 @@ hipError_t launch_residues(const Operand& a, const Operand& b, const Work& w, co
 // -> dst [planes][rows][q], plain row-major.
 // Grid-stride loop: the dispatch grid size counts work-items in 32 bits, so the launch is
 // capped and each thread walks the whole range.
-__global__ void unpermute_i8_kernel(const int8_t* __restrict__ src, int rows, int rows_pad, int q, int q_pad,
+__global__ void unpack_operands_kernel(const int8_t* __restrict__ src, int rows, int rows_pad, int q, int q_pad,
                                     int8_t* __restrict__ dst, long total) {
   const long stride = static_cast<long>(gridDim.x) * blockDim.x;
   for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
@@ -254,12 +254,12 @@ __global__ void unpermute_i8_kernel(const int8_t* __restrict__ src, int rows, in
   }
 }
 
-hipError_t launch_unpermute_i8(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
+hipError_t launch_unpack_operands(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
                                int8_t* dst, hipStream_t st) {
   const long total = static_cast<long>(planes) * rows * q;
   if (total <= 0) return hipSuccess;
   const long blocks = std::min<long>((total + 255) / 256, 1L << 20);
-  hipLaunchKernelGGL(unpermute_i8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, src, rows,
+  hipLaunchKernelGGL(unpack_operands_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, src, rows,
                      rows_pad, q, q_pad, dst, total);
   return hipGetLastError();
 }

@@ -62,8 +62,9 @@ enum {
 #define OZ2_MAX_S 20
 /* One INT32 dot product of int8 residues is exact while q 128^2 < 2^31, i.e. q < 2^17
  * ("Ozaki II supplement", section 1.3).  Longer inner dimensions are split into blocks of
- * 65536 whose partial products are reduced mod m_t before they are combined, which is
- * exact for any q; the limit below comes from the accu bound product, whose INT32 entries
+ * 2^17 whose partial products are reduced mod m_t before they are combined, which is exact
+ * for any q (odd m_t: residues are at most 127 in magnitude; m_t = 256: only the low byte
+ * of a block sum is used); the limit below comes from the accu bound product, whose INT32 entries
  * are at most q 64^2. */
 #define OZ2_MAX_Q 524287
 /* Largest q for which the raw P_t dump of ozaki2_dgemm_debug is defined (exact INT32). */

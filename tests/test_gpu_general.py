@@ -4,8 +4,8 @@
   result of ozaki2_dgemm on explicit copies of op(A), op(B) (same scalings, residues and
   CRT), and that result must match the oracle on op(A), op(B);
 * alpha / beta: C <- alpha C_hat + beta C as oracle.alpha_beta_update defines it;
-* q beyond 2^17: the GEMM folds its accumulators mod m every 65536 inner-dimension
-  bytes; d, b, R_t and X must stay bit-exact against the oracle.
+* q beyond 2^17: the GEMM runs over K-blocks of 2^17 and accumulates their residues mod
+  m_t; d, b, R_t and X must stay bit-exact against the oracle.
 """
 import numpy as np
 import pytest
@@ -84,7 +84,7 @@ def test_empty_inner_dimension_scales_c(oz):
 
 @pytest.mark.parametrize("mode", ["fast", "accu"])
 def test_k_blocked_inner_dimension(oz, mode):
-    """q = 131372: the GEMM folds its accumulators at stages 1023 and 2047."""
+    """q = 131372: two K-blocks (131072 + 300 inner-dimension elements)."""
     p, q, r, s = 40, 131372, 24, 8
     A = generate(p, q, 0.5, 71)
     B = generate(q, r, 0.5, 72)
