@@ -230,6 +230,9 @@ def main():
                     help="skip the context figures (native FP64 matmul, MFMA ceiling on random operands)")
     ap.add_argument("--cpu-rows", type=int, default=192)
     ap.add_argument("--cpu-cols", type=int, default=2048)
+    ap.add_argument("--zero-inputs", action="store_true",
+                    help="diagnostic: A = B = 0 (every residue plane is zero), to show the data-dependent "
+                         "power of the INT8 MFMAs; not a benchmark of the workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--sweep", action="store_true",
@@ -258,7 +261,11 @@ def main():
 
     w = WORKLOADS[args.workload]
     n, s, accu = w.n, w.s, w.mode == "accu"
-    A, B = w.inputs()
+    if args.zero_inputs:
+        A = np.zeros((n, n), order="F")
+        B = np.zeros((n, n), order="F")
+    else:
+        A, B = w.inputs()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     Ad = binding.colmajor(torch.from_numpy(np.ascontiguousarray(A)).to(dev))
@@ -328,7 +335,8 @@ def main():
         "baseline_ref": "pages: GH200 fast-14 n=8192, 72.1 effective TFLOPS (paper Table 3), other hardware",
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": w.name, "n": n, "mode": w.mode, "s": s, "phi": w.phi,
+        "config": {"workload": w.name + ("_zero_inputs" if args.zero_inputs else ""), "n": n, "mode": w.mode, "s": s,
+                   "phi": w.phi,
                    "seeds": [w.seed_a, w.seed_b], "inputs": "f64 column-major, resident in HBM"},
         "stages": stages,
         "roofline": {
@@ -348,7 +356,7 @@ def main():
         ctx["mfma_i8_ceiling_random_operands_tops"] = ceil_tops
         ctx["gemm_frac_of_mfma_ceiling"] = gemm_tops / ceil_tops
         result["context"] = ctx
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.zero_inputs:
         result["cpu_baseline"] = cpu_baseline(A, B, s, w.mode, args.cpu_rows, args.cpu_cols)
     else:
         result["cpu_baseline"] = None
