@@ -112,3 +112,58 @@ def test_p_dump_refused_when_k_blocked(oz):
     with pytest.raises(oz.Oz2Error) as info:
         oz.dgemm_debug(A, B, 8, "fast", want=("P",))
     assert info.value.status == oz.OZ2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_max_inner_dimension_max_s(oz, mode):
+    """q = OZ2_MAX_Q = 2^19 - 1 (four K-blocks) with s = 20."""
+    p, q, r, s = 8, oz.OZ2_MAX_Q, 8, 20
+    A = generate(p, q, 1.0, 81)
+    B = generate(q, r, 1.0, 82)
+    log(f"[max q] mode={mode} p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=("d", "b", "X"))
+    ref = oracle.ozaki2(A, B, s, mode)
+    assert_equal(out["d"].cpu().numpy(), ref["d"].astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), ref["b"].astype(np.int32), "b")
+    xg = out["X"].cpu().numpy()
+    for j in range(r):
+        for i in range(p):
+            assert x_limbs_to_int(xg[j, i]) == int(ref["X"][i, j]), f"X[{i},{j}]"
+    assert_chat_close(out["C"].cpu().numpy(), ref["C"], chat_tolerance(A, B, np.arange(p), np.arange(r)), "C")
+    log("[max q] ok")
+
+
+def test_accu_bound_product_at_its_int32_limit(oz):
+    """Every entry 2 - 2^-52 quantizes to 64, so the bound product is q 64^2 = 2147479552 at
+    q = OZ2_MAX_Q, the largest INT32 value the accu bound GEMM can meet."""
+    p, q, r, s = 4, oz.OZ2_MAX_Q, 4, 8
+    v = 2.0 - 2.0 ** -52
+    A = np.full((p, q), v, order="F")
+    B = np.full((q, r), -v, order="F")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, "accu", want=("rho", "gamma", "d", "b"))
+    assert (out["rho"].cpu().numpy() == q * 64 * 64).all()
+    assert (out["gamma"].cpu().numpy() == q * 64 * 64).all()
+    ref = oracle.ozaki2(A, B, s, "accu")
+    assert_equal(out["d"].cpu().numpy(), ref["d"].astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), ref["b"].astype(np.int32), "b")
+    assert_chat_close(out["C"].cpu().numpy(), ref["C"], chat_tolerance(A, B, np.arange(p), np.arange(r)), "C")
+
+
+@pytest.mark.parametrize("shape", [(1 << 23, 5, 3), (3, 5, 1 << 23)])
+def test_max_rows_or_columns(oz, shape):
+    """p or r at the largest accepted size, 2^23 (the launch grids at their widest)."""
+    p, q, r = shape
+    s = 2
+    A = generate(p, q, 0.5, 83)
+    B = generate(q, r, 0.5, 84)
+    log(f"[max dim] p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, "fast", want=("d", "b"))
+    rows = np.array(sorted({0, 1, p // 2, p - 2, p - 1}))
+    cols = np.array(sorted({0, 1, r // 2, r - 2, r - 1}))
+    ref = oracle.ozaki2_sample(A, B, s, "fast", rows, cols)
+    import torch
+    assert_equal(out["d"][torch.as_tensor(rows, device="cuda")].cpu().numpy(), ref["d"].astype(np.int32), "d")
+    assert_equal(out["b"][torch.as_tensor(cols, device="cuda")].cpu().numpy(), ref["b"].astype(np.int32), "b")
+    c = out["C"][torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")].cpu().numpy()
+    assert_chat_close(c, ref["C"], chat_tolerance(A, B, rows, cols), "C")
+    log("[max dim] ok")
