@@ -159,7 +159,7 @@ static void launch_crt_s(const Work& w, double* C, long ldc, double alpha, doubl
   const int groups = (w.p + kRowsPerThread - 1) / kRowsPerThread;
   if (groups == 0 || w.r == 0) return;
   const dim3 blocks(w.r, (groups + 255) / 256);
-  const long r_plane = static_cast<long>(w.r_pad) * w.p_pad;
+  const long r_plane = w.res_plane;
   if (dump.x != nullptr)
     hipLaunchKernelGGL((crt_kernel<S, true>), blocks, dim3(256), 0, st, w.res, r_plane, w.p_pad, w.p, w.r,
                        groups, w.d, w.b, C, ldc, alpha, beta, dump.x);

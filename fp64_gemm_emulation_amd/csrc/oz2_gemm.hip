@@ -38,17 +38,14 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 //                and the 8 first-half fragment reads of stage kt + 1 among the first 8.
 // At most 8 LDS reads are ever outstanding, so every wait is an exact count, and each
 // wait falls where the data has had half a stage of MFMAs to arrive.
-constexpr int kBM = 256;
-constexpr int kBN = 256;
 constexpr int kBK = kStageK;                    // 64 bytes of the inner dimension per stage
 constexpr int kStages = 4;
 constexpr int kTileBytes = kStageTile;          // 16 KiB per operand per stage
-constexpr int kStageBytes = 2 * kTileBytes;     // A then B
-constexpr int kLoadsPerStage = 8;               // global_load_lds per wave per stage (4 A + 4 B)
 constexpr int kGroupM = 4;  // tile rows per group of the XCD-aware launch order
 constexpr int kKBlock = 1 << 17;                // inner-dimension bytes per launch of the mod GEMM
+constexpr long kSmallTileBelow = 2 * 256;       // 256 x 256 tiles (all planes) below which 128 x 128 tiles run
 static_assert(static_cast<long>(kKBlock) * 127 * 127 < (1L << 31), "odd-modulus block products fit INT32");
-static_assert(kBM == kRowPad && kBN == kRowPad, "operand stage tiles are 256 rows");
+static_assert(kRowPad == 256, "operand stage tiles are 256 rows");
 
 // Constants of the output reduction R = P mod m for each modulus (index t).  The
 // accumulators start at -h (h = (m - 1) / 2 for odd m, 0 for m = 256), so the epilogue
@@ -131,16 +128,28 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 enum { kEpiMod = 0, kEpiRawMod = 1, kEpiBound = 2, kEpiModAcc = 3 };
 
-template <int EPI>
 // K: padded inner dimension (row length of the operand planes); stages kt0 .. kt0 + nk - 1
-// of it are multiplied.
-__global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restrict__ at, const int8_t* __restrict__ bt,
-                                                         long a_plane, long b_plane, int K, int kt0, int nk,
-                                                         uint8_t* __restrict__ res, long r_plane, int ldr,
-                                                         int32_t* __restrict__ p_dump, int p, int r,
-                                                         int* __restrict__ rho, int* __restrict__ gamma,
-                                                         int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStageBytes];
+// of it are multiplied.  TB: 32 x 32 MFMA blocks per wave and dimension; the workgroup
+// tile is 64 TB x 64 TB (TB = 4: 256 x 256, one workgroup per CU; TB = 2: 128 x 128 for
+// small products, two workgroups per CU so that one's epilogue overlaps the other's
+// MFMAs).  A 128-row tile reads one half of the 256-row stage tiles, which is contiguous.
+template <int EPI, int TB>
+__global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
+    const int8_t* __restrict__ at, const int8_t* __restrict__ bt, long a_plane, long b_plane, int K, int kt0, int nk,
+    uint8_t* __restrict__ res, long r_plane, int ldr, int32_t* __restrict__ p_dump, int p, int r,
+    int* __restrict__ rho, int* __restrict__ gamma, int tiles_m, int tiles_n) {
+  static_assert(TB == 4 || TB == 2, "tile shapes: 256 x 256 or 128 x 128");
+  constexpr int WT = 32 * TB;                // wave tile edge
+  constexpr int BT = 2 * WT;                 // workgroup tile edge
+  constexpr int kSlice = BT * kBK;           // bytes of one operand per stage in LDS
+  constexpr int kStageLds = 2 * kSlice;      // A then B
+  constexpr int kCopies = kSlice / 4 / 1024; // 1 KiB copies per wave and operand per stage (= TB)
+  constexpr int kLoads = 2 * kCopies;        // outstanding copy instructions per wave per stage
+  constexpr int kPairs = TB * TB / 2;        // MFMA pairs per 32-deep half
+  constexpr int kFeed = kPairs / 2 > 0 ? kPairs / 2 : 1;  // pairs that carry the reads / copies
+  constexpr int kReadsPer = 2 * TB / kFeed;  // fragment reads issued after each of those pairs
+  constexpr int kCopiesPer = kLoads / kFeed; // copies issued after each of those pairs
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStageLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in SGPRs
@@ -149,55 +158,57 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
   const int t = blockIdx.z;
   int tile_i, tile_j;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
-  const int i0 = tile_i * kBM;
-  const int j0 = tile_j * kBN;
+  const int i0 = tile_i * BT;
+  const int j0 = tile_j * BT;
 
-  // Copies: wave w moves bytes [4096 w + 1024 g, +1024) of each 16 KiB stage tile (g =
-  // 0..3 for A, again for B); lane l lands at byte 16 l of that KiB.
-  const int8_t* const ga = at + t * a_plane + static_cast<long>(tile_i) * kBM * K +
-                           static_cast<long>(kt0) * kTileBytes + wave * 4096 + 16 * lane;
-  const int8_t* const gb = bt + t * b_plane + static_cast<long>(tile_j) * kBN * K +
-                           static_cast<long>(kt0) * kTileBytes + wave * 4096 + 16 * lane;
+  // Copies: the tile's rows i0 .. i0 + BT - 1 lie in 256-row block i0 / 256 at byte offset
+  // 64 (i0 % 256) of each 16 KiB stage tile.  Wave w moves bytes [kSlice/4 w + 1024 g, +1024)
+  // of the tile's slice (g < kCopies for A, again for B); lane l lands at byte 16 l.
+  const long a_base = static_cast<long>(i0 / kRowPad) * kRowPad * K + (i0 % kRowPad) * kBK;
+  const long b_base = static_cast<long>(j0 / kRowPad) * kRowPad * K + (j0 % kRowPad) * kBK;
+  const int8_t* const ga = at + t * a_plane + a_base + static_cast<long>(kt0) * kTileBytes + wave * (kSlice / 4) + 16 * lane;
+  const int8_t* const gb = bt + t * b_plane + b_base + static_cast<long>(kt0) * kTileBytes + wave * (kSlice / 4) + 16 * lane;
   auto copy1 = [&](int kbuf, int ksrc, int g) {
-    const long src = static_cast<long>(ksrc) * kTileBytes + (g & 3) * 1024;
-    int8_t* dst = smem + (kbuf % kStages) * kStageBytes + wave * 4096 + (g & 3) * 1024;
-    if (g < 4)
+    const int c = g % kCopies;
+    const long src = static_cast<long>(ksrc) * kTileBytes + c * 1024;
+    int8_t* dst = smem + (kbuf % kStages) * kStageLds + wave * (kSlice / 4) + c * 1024;
+    if (g < kCopies)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(ga + src), (lds_ptr_t)dst, 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(gb + src), (lds_ptr_t)(dst + kTileBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(gb + src), (lds_ptr_t)(dst + kSlice), 16, 0, 0);
   };
 
   // Accumulators start at -h for the mod epilogues (see ModRed), at 0 for the bound.
   int init = 0;
   if constexpr (EPI != kEpiBound) init = -kModRed[t].h;
-  v16i acc[4][4];
+  v16i acc[TB][TB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < TB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < TB; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = init;
 
   // Fragment of a 32-row block for one 32-deep half: lane l reads row 32 blk + l % 32,
   // logical 16-byte chunk 2 half + l / 32 (the same for A and B, so the K positions that
-  // one MFMA pairs up agree).  f0 holds the first half's 4 A and 4 B fragments, f1 the
+  // one MFMA pairs up agree).  f0 holds the first half's TB A and TB B fragments, f1 the
   // second half's.
   const int frow = lane & 31;
   const int fsw = operand_swizzle(frow & 15);
   const int fk = lane >> 5;
-  const int8_t* const fa = smem + wm * 128 * kBK + frow * kBK;
-  const int8_t* const fb = smem + kTileBytes + wn * 128 * kBK + frow * kBK;
-  v4i f0[8], f1[8];
-  auto read1 = [&](int kbuf, int half, v4i (&x)[8], int g) {
-    const int off = (kbuf % kStages) * kStageBytes + 16 * ((2 * half + fk) ^ fsw);
-    if (g < 4) x[g] = *reinterpret_cast<const v4i*>(fa + off + g * 32 * kBK);
-    else x[g] = *reinterpret_cast<const v4i*>(fb + off + (g - 4) * 32 * kBK);
+  const int8_t* const fa = smem + wm * WT * kBK + frow * kBK;
+  const int8_t* const fb = smem + kSlice + wn * WT * kBK + frow * kBK;
+  v4i f0[2 * TB], f1[2 * TB];
+  auto read1 = [&](int kbuf, int half, v4i (&x)[2 * TB], int g) {
+    const int off = (kbuf % kStages) * kStageLds + 16 * ((2 * half + fk) ^ fsw);
+    if (g < TB) x[g] = *reinterpret_cast<const v4i*>(fa + off + g * 32 * kBK);
+    else x[g] = *reinterpret_cast<const v4i*>(fb + off + (g - TB) * 32 * kBK);
   };
-  // MFMA pair g (0..7) of a half: blocks (g / 2, 2 (g % 2)) and (g / 2, 2 (g % 2) + 1)
-  auto mfma2 = [&](const v4i (&x)[8], int g) {
-    const int mb = g >> 1, nb = 2 * (g & 1);
-    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[mb], x[4 + nb], acc[mb][nb], 0, 0, 0);
-    acc[mb][nb + 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[mb], x[5 + nb], acc[mb][nb + 1], 0, 0, 0);
+  // MFMA pair g of a half: blocks (g / (TB/2), 2 (g % (TB/2))) and the next column block
+  auto mfma2 = [&](const v4i (&x)[2 * TB], int g) {
+    const int mb = g / (TB / 2), nb = 2 * (g % (TB / 2));
+    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[mb], x[TB + nb], acc[mb][nb], 0, 0, 0);
+    acc[mb][nb + 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[mb], x[TB + nb + 1], acc[mb][nb + 1], 0, 0, 0);
   };
 
   if (nk > 0) {
@@ -206,44 +217,44 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
 #pragma unroll
     for (int kt = 0; kt < kStages; ++kt)
 #pragma unroll
-      for (int g = 0; g < kLoadsPerStage; ++g) copy1(kt, min(kt, nk - 1), g);
-    OZ2_WAIT_VMCNT((kStages - 1) * kLoadsPerStage);
+      for (int g = 0; g < kLoads; ++g) copy1(kt, min(kt, nk - 1), g);
+    OZ2_WAIT_VMCNT((kStages - 1) * kLoads);
     __builtin_amdgcn_s_barrier();
     OZ2_SCHED_FENCE();
 #pragma unroll
-    for (int g = 0; g < 8; ++g) read1(0, 0, f0, g);
+    for (int g = 0; g < 2 * TB; ++g) read1(0, 0, f0, g);
     OZ2_SCHED_FENCE();
     // The body is branch-free: the copy for stage kt + kStages is always issued, from
     // stage min(kt + kStages, nk - 1), into the buffer of stage kt, which nothing reads
     // after the middle barrier; so exactly kStages - 2 younger stages of copies are
-    // outstanding when a stage's copies are waited for.  Past the last stage, the first-half reads fetch a
-    // buffer that is not used again.
+    // outstanding when a stage's copies are waited for.  Past the last stage, the first-half
+    // reads fetch a buffer that is not used again.
     for (int kt = 0; kt < nk; ++kt) {
       OZ2_WAIT_LGKMCNT(0);
       OZ2_SCHED_FENCE();
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < kPairs; ++g) {
         mfma2(f0, g);
-        if (g < 4) {
-          read1(kt, 1, f1, 2 * g);
-          read1(kt, 1, f1, 2 * g + 1);
+        if (g < kFeed) {
+#pragma unroll
+          for (int u = 0; u < kReadsPer; ++u) read1(kt, 1, f1, kReadsPer * g + u);
         }
         OZ2_SCHED_FENCE();
       }
-      OZ2_WAIT_VMCNT((kStages - 2) * kLoadsPerStage);
+      OZ2_WAIT_VMCNT((kStages - 2) * kLoads);
       OZ2_WAIT_LGKMCNT(0);
       OZ2_SCHED_FENCE();
       __builtin_amdgcn_s_barrier();
       OZ2_SCHED_FENCE();
       const int kn = min(kt + kStages, nk - 1);
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < kPairs; ++g) {
         mfma2(f1, g);
-        if (g < 4) {
-          copy1(kt, kn, 2 * g);
-          copy1(kt, kn, 2 * g + 1);
-          read1(kt + 1, 0, f0, 2 * g);
-          read1(kt + 1, 0, f0, 2 * g + 1);
+        if (g < kFeed) {
+#pragma unroll
+          for (int u = 0; u < kCopiesPer; ++u) copy1(kt, kn, kCopiesPer * g + u);
+#pragma unroll
+          for (int u = 0; u < kReadsPer; ++u) read1(kt + 1, 0, f0, kReadsPer * g + u);
         }
         OZ2_SCHED_FENCE();
       }
@@ -254,31 +265,31 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
   }
 
   // acc[mb][nb][v] holds P_t[i][j] (minus h in the mod epilogues) with
-  //   i = i0 + 128 wm + 32 mb + 8 (v / 4) + 4 (lane / 32) + v % 4,
-  //   j = j0 + 128 wn + 32 nb + lane % 32.
-  const int ib = i0 + wm * 128 + 4 * (lane >> 5);
-  const int jb = j0 + wn * 128 + (lane & 31);
+  //   i = i0 + WT wm + 32 mb + 8 (v / 4) + 4 (lane / 32) + v % 4,
+  //   j = j0 + WT wn + 32 nb + lane % 32.
+  const int ib = i0 + wm * WT + 4 * (lane >> 5);
+  const int jb = j0 + wn * WT + (lane & 31);
   if constexpr (EPI == kEpiBound) {
-    // rows: max over this wave's 128 columns, then over the 32 lanes sharing lane / 32
+    // rows: max over this wave's columns, then over the 32 lanes sharing lane / 32
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < TB; ++mb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         int mx = 0;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) mx = max(mx, acc[mb][nb][v]);
+        for (int nb = 0; nb < TB; ++nb) mx = max(mx, acc[mb][nb][v]);
 #pragma unroll
         for (int off = 16; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, kWave));
         const int i = ib + mb * 32 + 8 * (v >> 2) + (v & 3);
         if ((lane & 31) == 0 && i < p) atomicMax(rho + i, mx);
       }
     }
-    // columns: max over this wave's 128 rows
+    // columns: max over this wave's rows
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < TB; ++nb) {
       int mx = 0;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < TB; ++mb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = max(mx, acc[mb][nb][v]);
       mx = max(mx, __shfl_xor(mx, 32, kWave));
@@ -290,9 +301,9 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
     uint8_t* rt = res + t * r_plane;
     const bool m256 = mr.m == 256;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < TB; ++mb) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < TB; ++nb) {
         const int j = jb + nb * 32;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -332,39 +343,58 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(const int8_t* __restric
   }
 }
 
-hipError_t launch_gemm(const Work& w, int epi, const DumpPtrs& dump, hipStream_t st) {
+template <int EPI, int TB>
+static void launch_tile(dim3 grid, hipStream_t st, const int8_t* a, const int8_t* b, long a_plane, long b_plane, int K,
+                        int kt0, int nk, uint8_t* res, long r_plane, int ldr, int32_t* pd, int p, int r, int* rho,
+                        int* gamma, int tiles_m, int tiles_n) {
+  hipLaunchKernelGGL((gemm_i8_kernel<EPI, TB>), grid, dim3(256), 0, st, a, b, a_plane, b_plane, K, kt0, nk, res,
+                     r_plane, ldr, pd, p, r, rho, gamma, tiles_m, tiles_n);
+}
+
+template <int TB>
+static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, hipStream_t st) {
+  constexpr int BT = 64 * TB;
   const int planes = epi == kEpiBound ? 1 : w.s;
-  const int tiles_m = w.p_pad / kBM;
-  const int tiles_n = w.r_pad / kBN;
+  const int tiles_m = w.p_pad / BT;
+  const int tiles_n = w.r_pad / BT;
   dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n), 1, planes);
-  const long a_plane = static_cast<long>(w.p_pad) * w.q_pad;
-  const long b_plane = static_cast<long>(w.r_pad) * w.q_pad;
-  const long r_plane = static_cast<long>(w.r_pad) * w.p_pad;
+  const long a_plane = w.at_plane;
+  const long b_plane = w.bt_plane;
+  const long r_plane = w.res_plane;
   const int nk = w.q_pad / kBK;
   if (epi == kEpiBound) {
-    hipLaunchKernelGGL(gemm_i8_kernel<kEpiBound>, grid, dim3(256), 0, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad,
-                       0, nk, nullptr, 0L, w.p_pad, nullptr, w.p, w.r, w.rho, w.gamma, tiles_m, tiles_n);
+    launch_tile<kEpiBound, TB>(grid, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad, 0, nk, nullptr, 0L, w.p_pad,
+                               nullptr, w.p, w.r, w.rho, w.gamma, tiles_m, tiles_n);
     return hipGetLastError();
   }
   if (epi != kEpiMod && epi != kEpiRawMod) return hipErrorInvalidValue;
   // the raw P_t dump covers one block only (the entry points refuse it for longer q)
-  if (epi == kEpiRawMod && nk > kKBlock / kBK) return hipErrorInvalidValue;
   constexpr int kBlockStages = kKBlock / kBK;
+  if (epi == kEpiRawMod && nk > kBlockStages) return hipErrorInvalidValue;
   for (int kt0 = 0; kt0 == 0 || kt0 < nk; kt0 += kBlockStages) {
     const int nkb = nk - kt0 < kBlockStages ? nk - kt0 : kBlockStages;
     if (kt0 > 0)
-      hipLaunchKernelGGL(gemm_i8_kernel<kEpiModAcc>, grid, dim3(256), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad,
-                         kt0, nkb, w.res, r_plane, w.p_pad, nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
+      launch_tile<kEpiModAcc, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, kt0, nkb, w.res, r_plane, w.p_pad,
+                                  nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
     else if (epi == kEpiRawMod)
-      hipLaunchKernelGGL(gemm_i8_kernel<kEpiRawMod>, grid, dim3(256), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad,
-                         0, nkb, w.res, r_plane, w.p_pad, dump.pt, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
+      launch_tile<kEpiRawMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
+                                  dump.pt, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
     else
-      hipLaunchKernelGGL(gemm_i8_kernel<kEpiMod>, grid, dim3(256), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad,
-                         0, nkb, w.res, r_plane, w.p_pad, nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
+      launch_tile<kEpiMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
+                               nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// 256 x 256 tiles unless that grid gives fewer than two workgroups per CU, where the
+// exposed per-tile prologue / epilogue and the partly empty last round dominate.
+hipError_t launch_gemm(const Work& w, int epi, const DumpPtrs& dump, hipStream_t st) {
+  const long planes = epi == kEpiBound ? 1 : w.s;
+  const long big_tiles = static_cast<long>(w.p_pad / 256) * (w.r_pad / 256) * planes;
+  if (big_tiles < kSmallTileBelow) return launch_gemm_tb<2>(w, epi, dump, st);
+  return launch_gemm_tb<4>(w, epi, dump, st);
 }
 
 }  // namespace oz2

@@ -28,6 +28,8 @@ struct Work {
   int* gamma;               // [r]   accu: column maxima of the bound product
   int8_t* at;               // s planes of p_pad x q_pad, tile-contiguous (operand_chunk_offset)
   int8_t* bt;               // s planes of r_pad x q_pad, same layout
+  long at_plane, bt_plane;  // byte strides between the planes of A_t / B_t
+  long res_plane;           // byte stride between the planes of R_t
   int8_t* abar;             // [p_pad][q_pad]     accu bound inputs (alias of A_t plane 0)
   int8_t* bbar;             // [r_pad][q_pad]     (alias of B_t plane 0)
   uint8_t* res;             // [s][r_pad][p_pad]  R_t, column-major planes
@@ -72,7 +74,7 @@ hipError_t launch_crt(const Work& w, double* C, long ldc, double alpha, double b
 
 // validation helper: operand planes in the tile-contiguous layout (padded) -> dst
 // [planes][rows][q], plain row-major
-hipError_t launch_unpack_operands(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
-                               int8_t* dst, hipStream_t st);
+hipError_t launch_unpack_operands(const int8_t* src, long plane_stride, int planes, int rows, int q, int q_pad,
+                                  int8_t* dst, hipStream_t st);
 
 }  // namespace oz2

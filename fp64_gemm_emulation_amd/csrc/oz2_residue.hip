@@ -185,8 +185,7 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __rest
 // dump[line dls + l dks].
 template <int S, int NL, bool DUMP>
 static void residues_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, const int* scale,
-                           int8_t* out, double* dump, long dls, long dks, hipStream_t st) {
-  const long plane = static_cast<long>(nlines_pad) * q_pad;
+                           int8_t* out, long plane, double* dump, long dls, long dks, hipStream_t st) {
   if (o.contig) {
     dim3 grid(nlines_pad / 16, q_pad / kKPad);
     hipLaunchKernelGGL((residues_cols_kernel<S, NL, DUMP>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, scale,
@@ -206,13 +205,13 @@ static void launch_residues_s(const Operand& a, const Operand& b, const Work& w,
   // A' dump: column-major p x q (ld p); B' dump: column-major q x r (ld q); each operand
   // runs the dumping kernel only when its own dump is requested
   if (dump.ap != nullptr)
-    residues_lines<S, NL, true>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, dump.ap, 1L, static_cast<long>(w.p), st);
+    residues_lines<S, NL, true>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, dump.ap, 1L, static_cast<long>(w.p), st);
   else
-    residues_lines<S, NL, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, nullptr, 0L, 0L, st);
+    residues_lines<S, NL, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, nullptr, 0L, 0L, st);
   if (dump.bp != nullptr)
-    residues_lines<S, NL, true>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, dump.bp, static_cast<long>(w.q), 1L, st);
+    residues_lines<S, NL, true>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, dump.bp, static_cast<long>(w.q), 1L, st);
   else
-    residues_lines<S, NL, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, nullptr, 0L, 0L, st);
+    residues_lines<S, NL, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, nullptr, 0L, 0L, st);
 }
 
 template <int S>
@@ -238,29 +237,28 @@ hipError_t launch_residues(const Operand& a, const Operand& b, const Work& w, co
   return hipGetLastError();
 }
 
-// Validation: src planes of rows_pad x q_pad bytes in the tile-contiguous operand layout
-// -> dst [planes][rows][q], plain row-major.
-// Grid-stride loop: the dispatch grid size counts work-items in 32 bits, so the launch is
-// capped and each thread walks the whole range.
-__global__ void unpack_operands_kernel(const int8_t* __restrict__ src, int rows, int rows_pad, int q, int q_pad,
-                                    int8_t* __restrict__ dst, long total) {
+// Validation: operand planes (tile-contiguous layout, plane_stride bytes apart) -> dst
+// [planes][rows][q], plain row-major.  Grid-stride loop: the dispatch grid size counts
+// work-items in 32 bits, so the launch is capped and each thread walks the whole range.
+__global__ void unpack_operands_kernel(const int8_t* __restrict__ src, long plane_stride, int rows, int q, int q_pad,
+                                       int8_t* __restrict__ dst, long total) {
   const long stride = static_cast<long>(gridDim.x) * blockDim.x;
   for (long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
     const int l = static_cast<int>(idx % q);
     const long rest = idx / q;
     const int row = static_cast<int>(rest % rows);
     const long plane = rest / rows;
-    dst[idx] = src[plane * rows_pad * q_pad + operand_elem_offset(row, l, q_pad)];
+    dst[idx] = src[plane * plane_stride + operand_elem_offset(row, l, q_pad)];
   }
 }
 
-hipError_t launch_unpack_operands(const int8_t* src, int planes, int rows, int rows_pad, int q, int q_pad,
-                               int8_t* dst, hipStream_t st) {
+hipError_t launch_unpack_operands(const int8_t* src, long plane_stride, int planes, int rows, int q, int q_pad,
+                                  int8_t* dst, hipStream_t st) {
   const long total = static_cast<long>(planes) * rows * q;
   if (total <= 0) return hipSuccess;
   const long blocks = std::min<long>((total + 255) / 256, 1L << 20);
-  hipLaunchKernelGGL(unpack_operands_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, src, rows,
-                     rows_pad, q, q_pad, dst, total);
+  hipLaunchKernelGGL(unpack_operands_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, src, plane_stride,
+                     rows, q, q_pad, dst, total);
   return hipGetLastError();
 }
 

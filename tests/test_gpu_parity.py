@@ -198,3 +198,22 @@ def test_workload_n16384_fast_s18(oz):
 
 def test_workload_n16384_accu_s18(oz):
     _sampled_case(oz, "n16384_accu_s18", nsamp=8)
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_large_tiles_on_ragged_shape(oz, mode):
+    """1800 x 300 x 1790 with s = 20: enough 256 x 256 tiles (8 x 8 x 20) for the large-tile
+    GEMM, whose ragged last tile row and column are sampled."""
+    import torch
+    p, q, r, s = 1800, 300, 1790, 20
+    A = generate(p, q, 1.0, 91)
+    B = generate(q, r, 1.0, 92)
+    want = ("d", "b", "Ap", "Bp", "At", "Bt", "P", "R", "X") + (("rho", "gamma", "Abar", "Bbar") if mode == "accu" else ())
+    log(f"[large tiles] mode={mode} p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=want)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(sample_indices(p, 10, 3).tolist()) | {1535, 1536, 1790, 1799}))
+    cols = np.array(sorted(set(sample_indices(r, 10, 4).tolist()) | {1535, 1536, 1780, 1789}))
+    ref = oracle.ozaki2_sample(A, B, s, mode, rows, cols)
+    compare_sampled(out, ref, A, B, s, mode, rows, cols)
+    log("[large tiles] ok")
