@@ -29,15 +29,23 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 //
 // K advances in stages of 64 bytes (two 32-deep halves).  Each stage tile of each operand
 // is a contiguous 16 KiB block in memory, copied into a ring of kStages LDS buffers with
-// global_load_lds_dwordx4 (1 KiB per instruction, no staging registers).  Per stage and
-// wave:
+// global_load_lds_dwordx4 (1 KiB per instruction, no staging registers).  Stage X lives
+// in buffer X mod kStages and is copied in two parts: its A slice during the second half
+// of stage X - kStages, its B slice during the first half of stage X - kStages + 1.  Per
+// stage kt and wave:
 //   first half:  wait for this half's fragments; 16 MFMAs, with the 8 fragment reads of
-//                the second half issued among the first 8;
-//   middle:      wait for the next stage's copies and the fragments; barrier;
-//   second half: 16 MFMAs, with the copy of stage kt + kStages into the buffer just released
-//                and the 8 first-half fragment reads of stage kt + 1 among the first 8.
+//                the second half among the first 8 and the B-slice copies of stage
+//                kt + kStages - 1 (into the buffer released at the previous middle barrier)
+//                after every second one;
+//   middle:      wait for both parts of stage kt + 1 and for the fragments; barrier;
+//   second half: 16 MFMAs, with the 8 first-half fragment reads of stage kt + 1 among the
+//                first 8 and the A-slice copies of stage kt + kStages (into the buffer of
+//                stage kt, released by this barrier) after every second one.
 // At most 8 LDS reads are ever outstanding, so every wait is an exact count, and each
-// wait falls where the data has had half a stage of MFMAs to arrive.
+// wait falls where the data has had half a stage of MFMAs to arrive.  Spreading the copies
+// over both halves, instead of issuing them all right after the barrier, keeps the four
+// waves from queueing their MFMAs behind 32 KiB of copies at the same moment: 3% faster
+// at n = 8192 and 10% at n = 16384.
 constexpr int kBK = kStageK;                    // 64 bytes of the inner dimension per stage
 constexpr int kStages = 4;
 constexpr int kTileBytes = kStageTile;          // 16 KiB per operand per stage
@@ -46,6 +54,7 @@ constexpr int kKBlock = 1 << 17;                // inner-dimension bytes per lau
 constexpr long kSmallTileBelow = 2 * 256;       // 256 x 256 tiles (all planes) below which 128 x 128 tiles run
 static_assert(static_cast<long>(kKBlock) * 127 * 127 < (1L << 31), "odd-modulus block products fit INT32");
 static_assert(kRowPad == 256, "operand stage tiles are 256 rows");
+static_assert(kStages == 4, "the copy schedule and its wait counts assume a ring of 4 stages");
 
 // Constants of the output reduction R = P mod m for each modulus (index t).  The
 // accumulators start at -h (h = (m - 1) / 2 for odd m, 0 for m = 256), so the epilogue
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
   constexpr int kPairs = TB * TB / 2;        // MFMA pairs per 32-deep half
   constexpr int kFeed = kPairs / 2 > 0 ? kPairs / 2 : 1;  // pairs that carry the reads / copies
   constexpr int kReadsPer = 2 * TB / kFeed;  // fragment reads issued after each of those pairs
-  constexpr int kCopiesPer = kLoads / kFeed; // copies issued after each of those pairs
+  constexpr int kCopyEvery = kPairs / kCopies;  // MFMA pairs per copy within one half
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStageLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -212,23 +221,27 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
   };
 
   if (nk > 0) {
-    // Prologue: stages 0..kStages-1 in flight (clamped to the last stage for short K),
-    // wait for stage 0, read its first-half fragments.
+    // Prologue: stages 0..kStages-2 and the A slice of stage kStages-1 in flight (clamped
+    // to the last stage for short K), wait for stage 0, read its first-half fragments.
 #pragma unroll
-    for (int kt = 0; kt < kStages; ++kt)
+    for (int kt = 0; kt < kStages - 1; ++kt)
 #pragma unroll
       for (int g = 0; g < kLoads; ++g) copy1(kt, min(kt, nk - 1), g);
-    OZ2_WAIT_VMCNT((kStages - 1) * kLoads);
+#pragma unroll
+    for (int g = 0; g < kCopies; ++g) copy1(kStages - 1, min(kStages - 1, nk - 1), g);
+    OZ2_WAIT_VMCNT((kStages - 2) * kLoads + kCopies);
     __builtin_amdgcn_s_barrier();
     OZ2_SCHED_FENCE();
 #pragma unroll
     for (int g = 0; g < 2 * TB; ++g) read1(0, 0, f0, g);
     OZ2_SCHED_FENCE();
-    // The body is branch-free: the copy for stage kt + kStages is always issued, from
-    // stage min(kt + kStages, nk - 1), into the buffer of stage kt, which nothing reads
-    // after the middle barrier; so exactly kStages - 2 younger stages of copies are
-    // outstanding when a stage's copies are waited for.  Past the last stage, the first-half
-    // reads fetch a buffer that is not used again.
+    // The body is branch-free: every copy is always issued, its source stage clamped to
+    // nk - 1, into a buffer that nothing reads any more (the B slice into the buffer of
+    // stage kt - 1, the A slice into that of stage kt, after the barriers that end their
+    // reads).  When stage kt + 1 is waited for in the middle of stage kt, the younger
+    // copies are exactly both parts of stages kt + 2 and kt + 3 (kStages = 4): 2 kLoads
+    // instructions.  Past the last stage, the first-half reads fetch a buffer that is not
+    // used again.
     for (int kt = 0; kt < nk; ++kt) {
       OZ2_WAIT_LGKMCNT(0);
       OZ2_SCHED_FENCE();
@@ -239,9 +252,11 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
 #pragma unroll
           for (int u = 0; u < kReadsPer; ++u) read1(kt, 1, f1, kReadsPer * g + u);
         }
+        if (g % kCopyEvery == kCopyEvery - 1)
+          copy1(kt + kStages - 1, min(kt + kStages - 1, nk - 1), kCopies + g / kCopyEvery);
         OZ2_SCHED_FENCE();
       }
-      OZ2_WAIT_VMCNT((kStages - 2) * kLoads);
+      OZ2_WAIT_VMCNT(2 * kLoads);
       OZ2_WAIT_LGKMCNT(0);
       OZ2_SCHED_FENCE();
       __builtin_amdgcn_s_barrier();
@@ -252,10 +267,9 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
         mfma2(f1, g);
         if (g < kFeed) {
 #pragma unroll
-          for (int u = 0; u < kCopiesPer; ++u) copy1(kt, kn, kCopiesPer * g + u);
-#pragma unroll
           for (int u = 0; u < kReadsPer; ++u) read1(kt + 1, 0, f0, kReadsPer * g + u);
         }
+        if (g % kCopyEvery == kCopyEvery - 1) copy1(kt, kn, g / kCopyEvery);
         OZ2_SCHED_FENCE();
       }
     }
