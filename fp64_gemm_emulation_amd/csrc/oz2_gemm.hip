@@ -314,41 +314,93 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
     const ModRed mr = kModRed[t];
     uint8_t* rt = res + t * r_plane;
     const bool m256 = mr.m == 256;
+    // residue bytes of rows i .. i + 3 (accumulator registers 4 g .. 4 g + 3) of column j,
+    // packed little-endian into one word; prev: the previous K-block's residues (kEpiModAcc)
+    auto residue_word = [&](int mb, int nb, int g, uint32_t prev) -> uint32_t {
+      uint32_t b0 = static_cast<uint32_t>(acc[mb][nb][4 * g]);
+      uint32_t b1 = static_cast<uint32_t>(acc[mb][nb][4 * g + 1]);
+      uint32_t b2 = static_cast<uint32_t>(acc[mb][nb][4 * g + 2]);
+      uint32_t b3 = static_cast<uint32_t>(acc[mb][nb][4 * g + 3]);
+      if constexpr (EPI == kEpiModAcc) {  // (P_block + R_prev) mod m: add the previous residue bytes
+        b0 += prev & 0xFFu;
+        b1 += (prev >> 8) & 0xFFu;
+        b2 += (prev >> 16) & 0xFFu;
+        b3 += prev >> 24;
+      }
+      if (!m256) {  // m = 256: P mod 256 is the low byte of P (h = 0)
+        b0 = mod_byte(static_cast<int>(b0), mr);
+        b1 = mod_byte(static_cast<int>(b1), mr);
+        b2 = mod_byte(static_cast<int>(b2), mr);
+        b3 = mod_byte(static_cast<int>(b3), mr);
+      }
+      const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+      const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+      return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+    };
+    if constexpr (EPI == kEpiMod) {
+      // The tile's BT x BT residue bytes go through LDS (the copy ring is free once every
+      // wave has passed its K loop and waited for its own copies) so that every store
+      // instruction writes whole 256-byte column segments: a lane's own words cover 32
+      // columns 8 bytes at a time.  Staging layout: word (il / 4) of tile column jl at
+      // word WC jl + ((il / 4) xor (jl mod 32)), so the 32 lanes of a half-wave, which hold
+      // 32 consecutive columns, write 32 distinct banks; a 16-byte read of logical chunk c
+      // finds its 4 words in chunk c xor ((jl mod 32) / 4), permuted by xor (jl mod 4).
+      constexpr int WC = BT / 4;            // words per tile column
+      static_assert(WC >= 32 && BT * BT <= kStages * kStageLds, "staging fits the ring");
+      uint32_t* const stage = reinterpret_cast<uint32_t*>(smem);
+      __builtin_amdgcn_s_barrier();
+      const int jl0 = wn * WT + (lane & 31);
+      const int wl0 = (wm * WT + 4 * (lane >> 5)) >> 2;
 #pragma unroll
-    for (int mb = 0; mb < TB; ++mb) {
+      for (int mb = 0; mb < TB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < TB; ++nb) {
-        const int j = jb + nb * 32;
+        for (int nb = 0; nb < TB; ++nb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int i = ib + mb * 32 + 8 * g;
-          uint32_t* const rp = reinterpret_cast<uint32_t*>(rt + static_cast<long>(j) * ldr + i);
-          uint32_t b0 = static_cast<uint32_t>(acc[mb][nb][4 * g]);
-          uint32_t b1 = static_cast<uint32_t>(acc[mb][nb][4 * g + 1]);
-          uint32_t b2 = static_cast<uint32_t>(acc[mb][nb][4 * g + 2]);
-          uint32_t b3 = static_cast<uint32_t>(acc[mb][nb][4 * g + 3]);
-          if constexpr (EPI == kEpiModAcc) {  // (P_block + R_prev) mod m: add the previous residue bytes
-            const uint32_t prev = *rp;
-            b0 += prev & 0xFFu;
-            b1 += (prev >> 8) & 0xFFu;
-            b2 += (prev >> 16) & 0xFFu;
-            b3 += prev >> 24;
+          for (int g = 0; g < 4; ++g) {
+            const int jl = jl0 + 32 * nb;
+            const int wl = wl0 + 8 * mb + 2 * g;
+            stage[WC * jl + (wl ^ (jl & 31))] = residue_word(mb, nb, g, 0u);
           }
-          if (!m256) {  // m = 256: P mod 256 is the low byte of P (h = 0)
-            b0 = mod_byte(static_cast<int>(b0), mr);
-            b1 = mod_byte(static_cast<int>(b1), mr);
-            b2 = mod_byte(static_cast<int>(b2), mr);
-            b3 = mod_byte(static_cast<int>(b3), mr);
-          }
-          const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
-          const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
-          *rp = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
-          if constexpr (EPI == kEpiRawMod) {
-            if (j < r) {
-              int32_t* dst = p_dump + (static_cast<long>(t) * r + j) * p;
+      __syncthreads();
+      constexpr int kTpc = BT / 16;         // threads per column (16 bytes each)
+      constexpr int kCols = 256 / kTpc;     // columns per pass of the workgroup
+      const int c = tid % kTpc;
+#pragma unroll 4
+      for (int pass = 0; pass < BT / kCols; ++pass) {
+        const int jl = pass * kCols + tid / kTpc;
+        const v4i d = *reinterpret_cast<const v4i*>(stage + WC * jl + 4 * (c ^ ((jl & 31) >> 2)));
+        const int sw = jl & 3;              // logical word k sits at position k xor sw
+        int x0 = d[0], x1 = d[1], x2 = d[2], x3 = d[3];
+        if (sw & 1) {
+          const int y0 = x0, y2 = x2;
+          x0 = x1; x1 = y0; x2 = x3; x3 = y2;
+        }
+        if (sw & 2) {
+          const int y0 = x0, y1 = x1;
+          x0 = x2; x1 = x3; x2 = y0; x3 = y1;
+        }
+        *reinterpret_cast<v4i*>(rt + static_cast<long>(j0 + jl) * ldr + i0 + 16 * c) = v4i{x0, x1, x2, x3};
+      }
+    } else {
 #pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (i + v < p) dst[i + v] = acc[mb][nb][4 * g + v] + mr.h;
+      for (int mb = 0; mb < TB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < TB; ++nb) {
+          const int j = jb + nb * 32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int i = ib + mb * 32 + 8 * g;
+            uint32_t* const rp = reinterpret_cast<uint32_t*>(rt + static_cast<long>(j) * ldr + i);
+            uint32_t prev = 0u;
+            if constexpr (EPI == kEpiModAcc) prev = *rp;
+            *rp = residue_word(mb, nb, g, prev);
+            if constexpr (EPI == kEpiRawMod) {
+              if (j < r) {
+                int32_t* dst = p_dump + (static_cast<long>(t) * r + j) * p;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  if (i + v < p) dst[i + v] = acc[mb][nb][4 * g + v] + mr.h;
+              }
             }
           }
         }
