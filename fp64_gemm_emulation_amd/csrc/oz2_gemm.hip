@@ -14,6 +14,8 @@
 // wrap-around preserves.  The accu bound product needs no blocking while q 2^12 < 2^31.  Operand planes are int8 in the tile-contiguous
 // layout of operand_chunk_offset (rows padded to 256, the inner dimension to 256 with
 // zeros), so the kernel needs no bounds checks in the K loop.
+#include <type_traits>
+
 #include "oz2_common.hpp"
 #include "oz2_internal.hpp"
 
@@ -111,6 +113,34 @@ __device__ __forceinline__ uint32_t mod_byte(int pp, const ModRed& mr) {
   return static_cast<uint32_t>(mad_i24(__float_as_int(y), -mr.m, z));
 }
 
+// Residue bytes of the four rows held in accumulator registers 4 g .. 4 g + 3 of one
+// 32 x 32 block, packed little-endian into one word.  prev: residue bytes of the previous
+// K-block to add (K-blocked launches), 0 otherwise.  M256: m = 256, where P mod 256 is the
+// low byte of P (h = 0).  A template parameter, so that the epilogue loops are straight-line
+// code for one modulus kind (a runtime test inside them is compiled into a branch per word).
+template <bool M256, bool ADD>
+__device__ __forceinline__ uint32_t residue_word(const v16i& a, int g, const ModRed& mr, uint32_t prev) {
+  uint32_t b0 = static_cast<uint32_t>(a[4 * g]);
+  uint32_t b1 = static_cast<uint32_t>(a[4 * g + 1]);
+  uint32_t b2 = static_cast<uint32_t>(a[4 * g + 2]);
+  uint32_t b3 = static_cast<uint32_t>(a[4 * g + 3]);
+  if constexpr (ADD) {
+    b0 += prev & 0xFFu;
+    b1 += (prev >> 8) & 0xFFu;
+    b2 += (prev >> 16) & 0xFFu;
+    b3 += prev >> 24;
+  }
+  if constexpr (!M256) {
+    b0 = mod_byte(static_cast<int>(b0), mr);
+    b1 = mod_byte(static_cast<int>(b1), mr);
+    b2 = mod_byte(static_cast<int>(b2), mr);
+    b3 = mod_byte(static_cast<int>(b3), mr);
+  }
+  const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Give
 // every XCD a contiguous range of tiles, and walk that range in groups of kGroupM tile
 // rows, so the workgroups resident on one XCD share A_t row panels and B_t column panels.
@@ -188,8 +218,14 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
   };
 
   // Accumulators start at -h for the mod epilogues (see ModRed), at 0 for the bound.
-  int init = 0;
-  if constexpr (EPI != kEpiBound) init = -kModRed[t].h;
+  // The modulus constants are loaded here and pinned in scalar registers: loaded in the
+  // epilogue, their latency would stall every wave at the end of every tile.
+  ModRed mr{0, 0, 0, 0.0f, 0.0f};
+  if constexpr (EPI != kEpiBound) {
+    mr = kModRed[t];
+    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
+  }
+  const int init = -mr.h;
   v16i acc[TB][TB];
 #pragma unroll
   for (int mb = 0; mb < TB; ++mb)
@@ -311,32 +347,8 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
       if (lane < 32 && j < r) atomicMax(gamma + j, mx);
     }
   } else {
-    const ModRed mr = kModRed[t];
     uint8_t* rt = res + t * r_plane;
     const bool m256 = mr.m == 256;
-    // residue bytes of rows i .. i + 3 (accumulator registers 4 g .. 4 g + 3) of column j,
-    // packed little-endian into one word; prev: the previous K-block's residues (kEpiModAcc)
-    auto residue_word = [&](int mb, int nb, int g, uint32_t prev) -> uint32_t {
-      uint32_t b0 = static_cast<uint32_t>(acc[mb][nb][4 * g]);
-      uint32_t b1 = static_cast<uint32_t>(acc[mb][nb][4 * g + 1]);
-      uint32_t b2 = static_cast<uint32_t>(acc[mb][nb][4 * g + 2]);
-      uint32_t b3 = static_cast<uint32_t>(acc[mb][nb][4 * g + 3]);
-      if constexpr (EPI == kEpiModAcc) {  // (P_block + R_prev) mod m: add the previous residue bytes
-        b0 += prev & 0xFFu;
-        b1 += (prev >> 8) & 0xFFu;
-        b2 += (prev >> 16) & 0xFFu;
-        b3 += prev >> 24;
-      }
-      if (!m256) {  // m = 256: P mod 256 is the low byte of P (h = 0)
-        b0 = mod_byte(static_cast<int>(b0), mr);
-        b1 = mod_byte(static_cast<int>(b1), mr);
-        b2 = mod_byte(static_cast<int>(b2), mr);
-        b3 = mod_byte(static_cast<int>(b3), mr);
-      }
-      const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
-      const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
-      return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
-    };
     if constexpr (EPI == kEpiMod) {
       // The tile's BT x BT residue bytes go through LDS (the copy ring is free once every
       // wave has passed its K loop and waited for its own copies) so that every store
@@ -351,16 +363,22 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
       __builtin_amdgcn_s_barrier();
       const int jl0 = wn * WT + (lane & 31);
       const int wl0 = (wm * WT + 4 * (lane >> 5)) >> 2;
+      auto stage_all = [&](auto m256) {
 #pragma unroll
-      for (int mb = 0; mb < TB; ++mb)
+        for (int mb = 0; mb < TB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < TB; ++nb)
+          for (int nb = 0; nb < TB; ++nb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int jl = jl0 + 32 * nb;
-            const int wl = wl0 + 8 * mb + 2 * g;
-            stage[WC * jl + (wl ^ (jl & 31))] = residue_word(mb, nb, g, 0u);
-          }
+            for (int g = 0; g < 4; ++g) {
+              const int jl = jl0 + 32 * nb;
+              const int wl = wl0 + 8 * mb + 2 * g;
+              stage[WC * jl + (wl ^ (jl & 31))] = residue_word<decltype(m256)::value, false>(acc[mb][nb], g, mr, 0u);
+            }
+      };
+      if (m256)
+        stage_all(std::true_type{});
+      else
+        stage_all(std::false_type{});
       __syncthreads();
       constexpr int kTpc = BT / 16;         // threads per column (16 bytes each)
       constexpr int kCols = 256 / kTpc;     // columns per pass of the workgroup
@@ -382,6 +400,8 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
         *reinterpret_cast<v4i*>(rt + static_cast<long>(j0 + jl) * ldr + i0 + 16 * c) = v4i{x0, x1, x2, x3};
       }
     } else {
+      // validation dump and K-blocked launches: direct 4-byte stores
+      auto store_all = [&](auto m256) {
 #pragma unroll
       for (int mb = 0; mb < TB; ++mb) {
 #pragma unroll
@@ -393,7 +413,7 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
             uint32_t* const rp = reinterpret_cast<uint32_t*>(rt + static_cast<long>(j) * ldr + i);
             uint32_t prev = 0u;
             if constexpr (EPI == kEpiModAcc) prev = *rp;
-            *rp = residue_word(mb, nb, g, prev);
+            *rp = residue_word<decltype(m256)::value, EPI == kEpiModAcc>(acc[mb][nb], g, mr, prev);
             if constexpr (EPI == kEpiRawMod) {
               if (j < r) {
                 int32_t* dst = p_dump + (static_cast<long>(t) * r + j) * p;
@@ -405,6 +425,11 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
           }
         }
       }
+      };
+      if (m256)
+        store_all(std::true_type{});
+      else
+        store_all(std::false_type{});
     }
   }
 }
