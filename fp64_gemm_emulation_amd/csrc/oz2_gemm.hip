@@ -141,6 +141,25 @@ __device__ __forceinline__ uint32_t residue_word(const v16i& a, int g, const Mod
   return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
 }
 
+// Residue word of a 16 x 16 block's accumulator registers (four consecutive rows of one
+// column), as residue_word for the 32 x 32 blocks.
+template <bool M256>
+__device__ __forceinline__ uint32_t residue_word4(const v4i& a, const ModRed& mr) {
+  uint32_t b0 = static_cast<uint32_t>(a[0]);
+  uint32_t b1 = static_cast<uint32_t>(a[1]);
+  uint32_t b2 = static_cast<uint32_t>(a[2]);
+  uint32_t b3 = static_cast<uint32_t>(a[3]);
+  if constexpr (!M256) {
+    b0 = mod_byte(static_cast<int>(b0), mr);
+    b1 = mod_byte(static_cast<int>(b1), mr);
+    b2 = mod_byte(static_cast<int>(b2), mr);
+    b3 = mod_byte(static_cast<int>(b3), mr);
+  }
+  const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Give
 // every XCD a contiguous range of tiles, and walk that range in groups of kGroupM tile
 // rows, so the workgroups resident on one XCD share A_t row panels and B_t column panels.
@@ -434,6 +453,154 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
   }
 }
 
+// The mod GEMM for large grids on v_mfma_i32_16x16x64_i8: 256 x 256 outputs per
+// workgroup, 8 waves (two per SIMD) in a 2 x 4 grid, each 128 x 64 outputs = 8 x 4 blocks
+// of 16 x 16 (128 accumulator registers, so two waves fit a SIMD and interleave their
+// MFMAs).  Under the board's power limit this form sustains more int8 operations per
+// second than one wave of 32x32x32 per SIMD: it reads and writes half the accumulator bytes
+// per multiply-add.  One stage (64 bytes of K) is one MFMA step for all 32 blocks.  Per
+// stage kt and wave: wait for this stage's fragments and for the copies of stage kt + 1;
+// barrier (after which nothing reads the buffer of stage kt); 32 MFMAs with the 12
+// fragment reads of stage kt + 1 after every second one of the first 24, and the 4 copies
+// of stage kt + kStages into the buffer of stage kt after MFMAs 4, 12, 20, 28.  The
+// younger copies when stage kt + 1 is waited for are those of stages kt + 2 and kt + 3.
+// Fragments: lane l reads row 16 b + l % 16 at logical chunk l / 16 of the stage (the
+// same for A and B, so the K positions one MFMA pairs up agree); the operand swizzle puts
+// the 16 rows of each chunk in distinct bank groups.  Accumulator register v of lane l of
+// a block holds row 4 (l / 16) + v, column l % 16.
+__global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restrict__ at, const int8_t* __restrict__ bt,
+                                                         long a_plane, long b_plane, int K, int nk,
+                                                         uint8_t* __restrict__ res, long r_plane, int ldr,
+                                                         int tiles_m, int tiles_n) {
+  constexpr int BT = 256;
+  constexpr int kSlice = BT * kBK;             // 16 KiB per operand per stage
+  constexpr int kStageLds = 2 * kSlice;        // A then B
+  constexpr int kWaves = 8;
+  constexpr int kCopiesW = kStageLds / 1024 / kWaves;  // 1 KiB copies per wave per stage (4)
+  constexpr int MB = 8, NB = 4;                // 16 x 16 blocks per wave
+  constexpr int kFr = MB + NB;                 // fragment reads per wave per stage (12)
+  static_assert(kCopiesW == 4 && kStages == 4, "copy schedule and wait counts");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStageLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;                    // rows 128 wm
+  const int wn = wave & 3;                     // columns 64 wn
+  const int t = blockIdx.z;
+  int tile_i, tile_j;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
+  const int i0 = tile_i * BT;
+  const int j0 = tile_j * BT;
+  ModRed mr = kModRed[t];
+  asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
+
+  // Copies: waves 0-3 move the A slice, waves 4-7 the B slice; wave w moves bytes
+  // [4096 (w mod 4) + 1024 c, +1024) of it, lane l at byte 16 l.
+  const int8_t* const gsrc = (wave < 4 ? at + t * a_plane + static_cast<long>(i0) * K
+                                       : bt + t * b_plane + static_cast<long>(j0) * K) +
+                             (wave & 3) * 4096 + 16 * lane;
+  int8_t* const gdst = smem + (wave >= 4 ? kSlice : 0) + (wave & 3) * 4096;
+  auto copy1 = [&](int kbuf, int ksrc, int c) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(gsrc + static_cast<long>(ksrc) * kTileBytes + c * 1024),
+                                     (lds_ptr_t)(gdst + (kbuf % kStages) * kStageLds + c * 1024), 16, 0, 0);
+  };
+  const int frow = lane & 15;
+  const int fch = (lane >> 4) ^ operand_swizzle(frow);
+  const int8_t* const fa = smem + (wm * 128 + frow) * kBK + 16 * fch;
+  const int8_t* const fb = smem + kSlice + (wn * 64 + frow) * kBK + 16 * fch;
+  auto read1 = [&](int kbuf, v4i (&x)[kFr], int g) {
+    const int off = (kbuf % kStages) * kStageLds;
+    if (g < MB) x[g] = *reinterpret_cast<const v4i*>(fa + off + g * 16 * kBK);
+    else x[g] = *reinterpret_cast<const v4i*>(fb + off + (g - MB) * 16 * kBK);
+  };
+  v4i acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4i{-mr.h, -mr.h, -mr.h, -mr.h};
+  v4i x0[kFr], x1[kFr];
+  // One stage: MFMAs on x, reads of stage kt + 1 into y, copies of stage kt + kStages.
+  auto stage = [&](int kt, v4i (&x)[kFr], v4i (&y)[kFr]) {
+    OZ2_WAIT_LGKMCNT(0);
+    OZ2_WAIT_VMCNT(2 * kCopiesW);
+    OZ2_SCHED_FENCE();
+    __builtin_amdgcn_s_barrier();
+    OZ2_SCHED_FENCE();
+    const int kn = min(kt + kStages, nk - 1);
+#pragma unroll
+    for (int u = 0; u < MB * NB; ++u) {
+      const int mb = u / NB, nb = u % NB;
+      acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mb], x[MB + nb], acc[mb][nb], 0, 0, 0);
+      if (u % 2 == 1 && u / 2 < kFr) read1(kt + 1, y, u / 2);
+      if (u % 8 == 4) copy1(kt, kn, u / 8);
+      OZ2_SCHED_FENCE();
+    }
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int kt = 0; kt < kStages; ++kt)
+#pragma unroll
+      for (int c = 0; c < kCopiesW; ++c) copy1(kt, min(kt, nk - 1), c);
+    OZ2_WAIT_VMCNT((kStages - 1) * kCopiesW);
+    __builtin_amdgcn_s_barrier();
+    OZ2_SCHED_FENCE();
+#pragma unroll
+    for (int g = 0; g < kFr; ++g) read1(0, x0, g);
+    OZ2_SCHED_FENCE();
+    // nk is a multiple of kStages (the inner dimension is padded to 256): even
+    for (int kt = 0; kt < nk; kt += 2) {
+      stage(kt, x0, x1);
+      stage(kt + 1, x1, x0);
+    }
+    OZ2_WAIT_VMCNT(0);
+    OZ2_WAIT_LGKMCNT(0);
+  }
+
+  // Epilogue: residue words through the (now free) LDS ring as in gemm_i8_kernel, so that
+  // every store instruction writes whole 256-byte column segments.
+  constexpr int WC = BT / 4;
+  uint32_t* const stg = reinterpret_cast<uint32_t*>(smem);
+  __builtin_amdgcn_s_barrier();
+  const int jl0 = wn * 64 + (lane & 15);
+  const int wl0 = wm * 32 + (lane >> 4);
+  auto stage_all = [&](auto m256) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int jl = jl0 + 16 * nb;
+        const int wl = wl0 + 4 * mb;
+        stg[WC * jl + (wl ^ (jl & 31))] = residue_word4<decltype(m256)::value>(acc[mb][nb], mr);
+      }
+  };
+  if (mr.m == 256)
+    stage_all(std::true_type{});
+  else
+    stage_all(std::false_type{});
+  __syncthreads();
+  uint8_t* const rt = res + t * r_plane;
+  constexpr int kTpc = BT / 16;                // threads per column
+  constexpr int kCols = 512 / kTpc;            // columns per pass
+  const int c = tid % kTpc;
+#pragma unroll 4
+  for (int pass = 0; pass < BT / kCols; ++pass) {
+    const int jl = pass * kCols + tid / kTpc;
+    const v4i d = *reinterpret_cast<const v4i*>(stg + WC * jl + 4 * (c ^ ((jl & 31) >> 2)));
+    const int sw = jl & 3;
+    int x0w = d[0], x1w = d[1], x2w = d[2], x3w = d[3];
+    if (sw & 1) {
+      const int y0 = x0w, y2 = x2w;
+      x0w = x1w; x1w = y0; x2w = x3w; x3w = y2;
+    }
+    if (sw & 2) {
+      const int y0 = x0w, y1 = x1w;
+      x0w = x2w; x1w = x3w; x2w = y0; x3w = y1;
+    }
+    *reinterpret_cast<v4i*>(rt + static_cast<long>(j0 + jl) * ldr + i0 + 16 * c) = v4i{x0w, x1w, x2w, x3w};
+  }
+}
+
 template <int EPI, int TB>
 static void launch_tile(dim3 grid, hipStream_t st, const int8_t* a, const int8_t* b, long a_plane, long b_plane, int K,
                         int kt0, int nk, uint8_t* res, long r_plane, int ldr, int32_t* pd, int p, int r, int* rho,
@@ -470,6 +637,9 @@ static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, h
     else if (epi == kEpiRawMod)
       launch_tile<kEpiRawMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
                                   dump.pt, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
+    else if constexpr (TB == 4)
+      hipLaunchKernelGGL(gemm_w8_kernel, grid, dim3(512), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad, nkb, w.res,
+                         r_plane, w.p_pad, tiles_m, tiles_n);
     else
       launch_tile<kEpiMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
                                nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
