@@ -38,7 +38,7 @@ def measured_traffic(workload):
     counters on a plain device copy of known size, and the SHA-256 of the GEMM source it
     was taken with; a different source means the figure is stale and None is returned.
     """
-    path = os.path.join(ROOT, "profiles", f"gemm_i8_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"gemm_w8_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -113,8 +113,8 @@ def mfma_ceiling(blocks=1024, rounds=3584, reps=5):
     lib.oz2calib_mfma_i8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.oz2calib_mfma_i8.restype = ctypes.c_int
     gen = torch.Generator(device="cuda").manual_seed(7)
-    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (blocks * 8 * 256 * 4,), dtype=torch.int32, device="cuda", generator=gen)
-    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (blocks * 8 * 512 * 4,), dtype=torch.int32, device="cuda", generator=gen)
+    out = torch.empty(blocks * 512, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     call = lambda: lib.oz2calib_mfma_i8(src.data_ptr(), blocks, rounds, out.data_ptr(), stream.cuda_stream)
     assert call() == 0
@@ -126,7 +126,7 @@ def mfma_ceiling(blocks=1024, rounds=3584, reps=5):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    ops = blocks * 4 * 16 * 32768 * 2.0 * rounds
+    ops = blocks * 8 * 16 * 16384 * 2.0 * rounds  # 2^21 multiply-adds per block and round
     return ops / (ms * 1e-3) / 1e12
 
 
@@ -341,7 +341,7 @@ def main():
         "stages": stages,
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_i8_kernel (s batched INT8 GEMMs + mod epilogue)",
+            "kernel": "gemm_w8_kernel (s batched INT8 GEMMs + mod epilogue)",
             "achieved": gemm_tops,
             "peak": PEAK_INT8_TOPS,
             "unit": "TFLOP/s",

@@ -1,53 +1,55 @@
 // mfma_ceiling.hip -- measurement aid, not part of the GEMM emulation: the sustained
-// rate of v_mfma_i32_32x32x32_i8 issued from registers only, one wave per SIMD, four
-// waves per workgroup, 16 independent 32x32 accumulators per wave.  The operands are
-// random bytes that change every round (byte rotations, a handful of VALU instructions
-// per 16 MFMAs), as the operands of the modular GEMMs do; with constant or zero operands
-// the matrix cores draw less power and run faster, so those would overstate what a
-// GEMM on residues can reach.  Used by bench.py for the power-limited MFMA ceiling.
+// rate of v_mfma_i32_16x16x64_i8 issued from registers only, in the form the large-grid
+// mod GEMM uses it (eight waves per workgroup, two per SIMD, 16 independent 16x16
+// accumulators per wave).  The operands are random bytes that change every round (byte
+// rotations, a handful of VALU instructions per 16 MFMAs), as the operands of the modular
+// GEMMs do; with constant or zero operands the matrix cores draw less power and run
+// faster, so those would overstate what a GEMM on residues can reach.  Used by bench.py
+// for the power-limited MFMA ceiling.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(256, 1) void mfma_i8_ceiling_kernel(const v4i* __restrict__ src, int rounds,
+__device__ __forceinline__ v4i rotate_bytes(v4i x) {
+  return v4i{static_cast<int>(__builtin_amdgcn_alignbyte(x[1], x[0], 1)),
+             static_cast<int>(__builtin_amdgcn_alignbyte(x[2], x[1], 1)),
+             static_cast<int>(__builtin_amdgcn_alignbyte(x[3], x[2], 1)),
+             static_cast<int>(__builtin_amdgcn_alignbyte(x[0], x[3], 1))};
+}
+
+__global__ __launch_bounds__(512, 1) void mfma_i8_ceiling_kernel(const v4i* __restrict__ src, int rounds,
                                                                    int* __restrict__ out) {
   const int tid = threadIdx.x;
   v4i f[8];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) f[g] = src[(blockIdx.x * 8 + g) * 256 + tid];
-  v16i acc[16];
+  for (int g = 0; g < 8; ++g) f[g] = src[(blockIdx.x * 8 + g) * 512 + tid];
+  v4i acc[16];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = v16i{};
+  for (int k = 0; k < 16; ++k) acc[k] = v4i{};
   for (int it = 0; it < rounds; ++it) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        acc[mb * 4 + nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[mb], f[4 + nb], acc[mb * 4 + nb], 0, 0, 0);
+        acc[mb * 4 + nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[mb], f[4 + nb], acc[mb * 4 + nb], 0, 0, 0);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const v4i x = f[g];
-      f[g] = v4i{static_cast<int>(__builtin_amdgcn_alignbyte(x[1], x[0], 1)),
-                 static_cast<int>(__builtin_amdgcn_alignbyte(x[2], x[1], 1)),
-                 static_cast<int>(__builtin_amdgcn_alignbyte(x[3], x[2], 1)),
-                 static_cast<int>(__builtin_amdgcn_alignbyte(x[0], x[3], 1))};
-    }
+    for (int g = 0; g < 8; ++g) f[g] = rotate_bytes(f[g]);
   }
   int x = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) x ^= acc[k][v];
-  out[blockIdx.x * 256 + tid] = x;
+    for (int v = 0; v < 4; ++v) x ^= acc[k][v];
+  out[blockIdx.x * 512 + tid] = x;
 }
 
-// src: blocks * 8 * 256 16-byte random words (device); out: blocks * 256 ints (device).
-// One round is 16 MFMAs of 32 x 32 x 32 per wave: 4 * 16 * 32768 multiply-adds per block.
+// src: blocks * 8 * 512 16-byte random words (device); out: blocks * 512 ints (device).
+// One round is 16 MFMAs of 16 x 16 x 64 per wave, 8 waves: 8 * 16 * 16384 = 2^21
+// multiply-adds per block.
 extern "C" int oz2calib_mfma_i8(const void* src, int blocks, int rounds, int* out, void* stream) {
   if (!src || !out || blocks <= 0 || rounds <= 0) return 1;
-  hipLaunchKernelGGL(mfma_i8_ceiling_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(mfma_i8_ceiling_kernel, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream),
                      static_cast<const v4i*>(src), rounds, out);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -468,10 +468,15 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
 // same for A and B, so the K positions one MFMA pairs up agree); the operand swizzle puts
 // the 16 rows of each chunk in distinct bank groups.  Accumulator register v of lane l of
 // a block holds row 4 (l / 16) + v, column l % 16.
+// EPI: kEpiMod (residues R_t) or kEpiBound (the accu bound product: row and column maxima
+// of the single plane, accumulators from 0).
+template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restrict__ at, const int8_t* __restrict__ bt,
                                                          long a_plane, long b_plane, int K, int nk,
                                                          uint8_t* __restrict__ res, long r_plane, int ldr,
+                                                         int* __restrict__ rho, int* __restrict__ gamma, int p, int r,
                                                          int tiles_m, int tiles_n) {
+  static_assert(EPI == kEpiMod || EPI == kEpiBound, "epilogues of the 8-wave GEMM");
   constexpr int BT = 256;
   constexpr int kSlice = BT * kBK;             // 16 KiB per operand per stage
   constexpr int kStageLds = 2 * kSlice;        // A then B
@@ -491,8 +496,11 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
   tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
   const int i0 = tile_i * BT;
   const int j0 = tile_j * BT;
-  ModRed mr = kModRed[t];
-  asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
+  ModRed mr{0, 0, 0, 0.0f, 0.0f};
+  if constexpr (EPI == kEpiMod) {
+    mr = kModRed[t];
+    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
+  }
 
   // Copies: waves 0-3 move the A slice, waves 4-7 the B slice; wave w moves bytes
   // [4096 (w mod 4) + 1024 c, +1024) of it, lane l at byte 16 l.
@@ -557,6 +565,36 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
     OZ2_WAIT_LGKMCNT(0);
   }
 
+  if constexpr (EPI == kEpiBound) {
+    // rows: max over this wave's 4 column blocks, then over the 16 lanes of each row group
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        int mx = 0;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) mx = max(mx, acc[mb][nb][v]);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, kWave));
+        const int i = i0 + wm * 128 + 16 * mb + 4 * (lane >> 4) + v;
+        if ((lane & 15) == 0 && i < p) atomicMax(rho + i, mx);
+      }
+    }
+    // columns: max over this wave's 8 row blocks and 4 registers, then over the 4 row groups
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int mx = 0;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mx = max(mx, acc[mb][nb][v]);
+      mx = max(mx, __shfl_xor(mx, 16, kWave));
+      mx = max(mx, __shfl_xor(mx, 32, kWave));
+      const int j = j0 + wn * 64 + 16 * nb + (lane & 15);
+      if (lane < 16 && j < r) atomicMax(gamma + j, mx);
+    }
+    return;
+  }
   // Epilogue: residue words through the (now free) LDS ring as in gemm_i8_kernel, so that
   // every store instruction writes whole 256-byte column segments.
   constexpr int WC = BT / 4;
@@ -621,8 +659,12 @@ static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, h
   const long r_plane = w.res_plane;
   const int nk = w.q_pad / kBK;
   if (epi == kEpiBound) {
-    launch_tile<kEpiBound, TB>(grid, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad, 0, nk, nullptr, 0L, w.p_pad,
-                               nullptr, w.p, w.r, w.rho, w.gamma, tiles_m, tiles_n);
+    if constexpr (TB == 4)
+      hipLaunchKernelGGL(gemm_w8_kernel<kEpiBound>, grid, dim3(512), 0, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad,
+                         nk, nullptr, 0L, w.p_pad, w.rho, w.gamma, w.p, w.r, tiles_m, tiles_n);
+    else
+      launch_tile<kEpiBound, TB>(grid, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad, 0, nk, nullptr, 0L, w.p_pad,
+                                 nullptr, w.p, w.r, w.rho, w.gamma, tiles_m, tiles_n);
     return hipGetLastError();
   }
   if (epi != kEpiMod && epi != kEpiRawMod) return hipErrorInvalidValue;
@@ -638,8 +680,8 @@ static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, h
       launch_tile<kEpiRawMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
                                   dump.pt, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
     else if constexpr (TB == 4)
-      hipLaunchKernelGGL(gemm_w8_kernel, grid, dim3(512), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad, nkb, w.res,
-                         r_plane, w.p_pad, tiles_m, tiles_n);
+      hipLaunchKernelGGL(gemm_w8_kernel<kEpiMod>, grid, dim3(512), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad, nkb,
+                         w.res, r_plane, w.p_pad, nullptr, nullptr, w.p, w.r, tiles_m, tiles_n);
     else
       launch_tile<kEpiMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
                                nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
