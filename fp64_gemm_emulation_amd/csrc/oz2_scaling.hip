@@ -87,78 +87,107 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const double* __restric
   }
 }
 
-// Contiguous lines (columns of B, or rows of op(A) = A^T): one wave per (line j, block c);
-// lane reads l = c kChunk + lane + 64 k, k = 0..3, so every load instruction is 512
-// contiguous bytes.
+// Contiguous lines (columns of B, or rows of op(A) = A^T): one wave per line j and
+// kColBlocks consecutive blocks c; for each block, lane reads l = c kChunk + lane + 64 k,
+// k = 0..3, so every load instruction is 512 contiguous bytes, and all of the wave's loads
+// are issued before the first block is reduced.  (One wave per block made 65536 tiny
+// workgroups at n = 8192, which the dispatcher could not launch fast enough.)
+constexpr int kColBlocks = 8;
 template <bool MAXONLY>
 __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                          int nch, int* __restrict__ part_e,
                                                          double* __restrict__ part_s,
                                                          unsigned* __restrict__ flags) {
-  // grid: x = column j, y = groups of 4 blocks; one wave per (j, c)
+  // grid: x = column j, y = groups of 4 kColBlocks blocks; one wave per (j, kColBlocks blocks)
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x;
-  const int c = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (c >= nch) return;  // whole wave
+  const int c0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kColBlocks;
+  if (c0 >= nch) return;  // whole wave
   const double* col = B + static_cast<long>(j) * ldb;
-  double v[4];
-  int emax = kNoExp;
+  double v[kColBlocks][4];
   bool bad = false;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int l = c * kChunk + lane + kWave * k;
-    double x = l < q ? col[l] : 0.0;
-    const bool nf = is_nonfinite(x);
-    bad |= nf;
-    x = nf ? 0.0 : x;
-    v[k] = x;
-    emax = max(emax, exponent_of(x));
-  }
-  if (bad) atomicOr(flags, kFlagNonFinite);
-  const int ec = wave_max(emax);
-  const long slot = static_cast<long>(j) * nch + c;
-  if constexpr (MAXONLY) {
-    if (lane == 0) part_e[slot] = ec;
-  } else {
-    double acc = 0.0;
-    if (ec != kNoExp) {
+  for (int b = 0; b < kColBlocks; ++b)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const double u = ceil_scaled_abs(v[k], exponent_of(v[k]), kFBits - ec);
-        acc = fma(u, u, acc);
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int l = (c0 + b) * kChunk + lane + kWave * k;
+      double x = (c0 + b < nch && l < q) ? col[l] : 0.0;
+      const bool nf = is_nonfinite(x);
+      bad |= nf;
+      v[b][k] = nf ? 0.0 : x;
     }
-    acc = wave_sum(acc);  // exact: at most 256 * 2^40
-    if (lane == 0) {
-      part_e[slot] = ec;
-      part_s[slot] = acc;
+  if (bad) atomicOr(flags, kFlagNonFinite);
+#pragma unroll
+  for (int b = 0; b < kColBlocks; ++b) {
+    const int c = c0 + b;
+    if (c >= nch) break;  // whole wave
+    int emax = kNoExp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) emax = max(emax, exponent_of(v[b][k]));
+    const int ec = wave_max(emax);
+    const long slot = static_cast<long>(j) * nch + c;
+    if constexpr (MAXONLY) {
+      if (lane == 0) part_e[slot] = ec;
+    } else {
+      double acc = 0.0;
+      if (ec != kNoExp) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const double u = ceil_scaled_abs(v[b][k], exponent_of(v[b][k]), kFBits - ec);
+          acc = fma(u, u, acc);
+        }
+      }
+      acc = wave_sum(acc);  // exact: at most 256 * 2^40
+      if (lane == 0) {
+        part_e[slot] = ec;
+        part_s[slot] = acc;
+      }
     }
   }
 }
 
-// One thread per line (rows of A first, then columns of B): combine block partials.
-__global__ void fast_exponents_kernel(int na, int nb, int nch, const int* __restrict__ pe_a,
-                                      const double* __restrict__ ps_a, const int* __restrict__ pe_b,
-                                      const double* __restrict__ ps_b, int* __restrict__ d,
-                                      int* __restrict__ b, int tau) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= na + nb) return;
+// One wave per line (rows of A first, then columns of B): combine the block partials, the
+// lanes taking blocks lane, lane + 64, ...  S is exact in uint64 (at most q 2^40 < 2^59).
+__global__ __launch_bounds__(256) void fast_exponents_kernel(int na, int nb, int nch, const int* __restrict__ pe_a,
+                                                             const double* __restrict__ ps_a,
+                                                             const int* __restrict__ pe_b,
+                                                             const double* __restrict__ ps_b, int* __restrict__ d,
+                                                             int* __restrict__ b, int tau) {
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= na + nb) return;  // whole wave
   const bool is_a = idx < na;
   const int line = is_a ? idx : idx - na;
   const int* pe = (is_a ? pe_a : pe_b) + static_cast<long>(line) * nch;
   const double* ps = (is_a ? ps_a : ps_b) + static_cast<long>(line) * nch;
   int e = kNoExp;
-  for (int c = 0; c < nch; ++c) e = max(e, pe[c]);
+  for (int c = lane; c < nch; c += kWave) e = max(e, pe[c]);
+  e = wave_max(e);
   int out = 0;
   if (e != kNoExp) {
     uint64_t S = 0;
-    for (int c = 0; c < nch; ++c) S += ceil_shift(ps[c], 2 * (e - pe[c]));
+    for (int c = lane; c < nch; c += kWave) {
+      const int ec = pe[c];
+      if (ec != kNoExp) S += ceil_shift(ps[c], 2 * (e - ec));
+    }
+    uint32_t lo = static_cast<uint32_t>(S), hi = static_cast<uint32_t>(S >> 32);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t lo2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off, kWave));
+      const uint32_t hi2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off, kWave));
+      const uint32_t sum = lo + lo2;
+      hi = hi + hi2 + (sum < lo ? 1u : 0u);
+      lo = sum;
+    }
+    S = (static_cast<uint64_t>(hi) << 32) | lo;
     out = ((tau - clog2_u64(S)) >> 1) + kFBits - e;
   }
-  if (is_a)
-    d[line] = out;
-  else
-    b[line] = out;
+  if (lane == 0) {
+    if (is_a)
+      d[line] = out;
+    else
+      b[line] = out;
+  }
 }
 
 // accu: line max-abs exponents from block maxima.
@@ -270,7 +299,7 @@ static void stats_lines(const Operand& o, int nlines, int q, int nch, int* pe, d
                         hipStream_t st) {
   if (nch == 0 || nlines == 0) return;
   if (o.contig) {
-    dim3 grid(nlines, blocks_for(nch, 4));
+    dim3 grid(nlines, blocks_for(nch, 4 * kColBlocks));
     hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps, flags);
   } else {
     dim3 grid(blocks_for(nlines, kWave), nch);
@@ -289,7 +318,7 @@ hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w
   hipError_t e = launch_stats<false>(a, b, w, st);
   if (e != hipSuccess) return e;
   const int n = w.p + w.r;
-  hipLaunchKernelGGL(fast_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.nch,
+  hipLaunchKernelGGL(fast_exponents_kernel, dim3(blocks_for(n, 4)), dim3(256), 0, st, w.p, w.r, w.nch,
                      w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b, w.d, w.b, w.tau);
   return hipGetLastError();
 }
