@@ -103,12 +103,15 @@ def compare_sampled(out, ref, A, B, s, mode, rows, cols):
     assert_equal(bp, ref["Bp"], "B'")
     at = out["At"][:, rows_t, :].cpu().numpy()
     bt = out["Bt"][:, cols_t, :].cpu().numpy()
-    pt = out["P"][:, cols_t][:, :, rows_t].cpu().numpy()
+    # P_t is dumped only when requested; the GEMM launch then runs the kernel form that
+    # writes the raw products, so runs without it check the production GEMM's R_t
+    pt = out["P"][:, cols_t][:, :, rows_t].cpu().numpy() if "P" in out else None
     rt = out["R"][:, cols_t][:, :, rows_t].cpu().numpy()
     for t in range(s):
         assert_equal(at[t], ref["At"][t].astype(np.int8), f"A_t t={t}")
         assert_equal(bt[t], ref["Bt"][t].T.astype(np.int8), f"B_t t={t}")
-        assert_equal(pt[t], ref["P"][t].T.astype(np.int32), f"P_t t={t}")
+        if pt is not None:
+            assert_equal(pt[t], ref["P"][t].T.astype(np.int32), f"P_t t={t}")
         assert_equal(rt[t], ref["R"][t].T.astype(np.uint8), f"R_t t={t}")
     xg = out["X"][cols_t][:, rows_t].cpu().numpy()
     for jj in range(len(cols)):

@@ -160,7 +160,9 @@ def _sampled_case(oz, name, nsamp=12):
     w = WORKLOADS[name]
     log(f"[sampled] {name}: generating inputs n={w.n}")
     A, B = w.inputs()
-    want = ("d", "b", "Ap", "Bp", "At", "Bt", "P", "R", "X") + (("rho", "gamma", "Abar", "Bbar") if w.mode == "accu" else ())
+    # no raw P_t dump: the GEMM then runs exactly as in ozaki2_dgemm (the large-grid
+    # 16x16x64 kernel), and its R_t, X and C are compared
+    want = ("d", "b", "Ap", "Bp", "At", "Bt", "R", "X") + (("rho", "gamma", "Abar", "Bbar") if w.mode == "accu" else ())
     log(f"[sampled] {name}: GPU run s={w.s} mode={w.mode}")
     out = oz.dgemm_debug(to_device(A), to_device(B), w.s, w.mode, want=want)
     torch.cuda.synchronize()
@@ -200,16 +202,19 @@ def test_workload_n16384_accu_s18(oz):
     _sampled_case(oz, "n16384_accu_s18", nsamp=8)
 
 
+@pytest.mark.parametrize("raw_p", [False, True])
 @pytest.mark.parametrize("mode", ["fast", "accu"])
-def test_large_tiles_on_ragged_shape(oz, mode):
-    """1800 x 300 x 1790 with s = 20: enough 256 x 256 tiles (8 x 8 x 20) for the large-tile
-    GEMM, whose ragged last tile row and column are sampled."""
+def test_large_tiles_on_ragged_shape(oz, mode, raw_p):
+    """1800 x 300 x 1790 with s = 20: enough 256 x 256 tiles (8 x 8 x 20) for the large-grid
+    GEMM, whose ragged last tile row and column are sampled.  Without the raw P_t dump the
+    production 16x16x64 kernel runs; with it, the kernel form that also writes P_t."""
     import torch
     p, q, r, s = 1800, 300, 1790, 20
     A = generate(p, q, 1.0, 91)
     B = generate(q, r, 1.0, 92)
-    want = ("d", "b", "Ap", "Bp", "At", "Bt", "P", "R", "X") + (("rho", "gamma", "Abar", "Bbar") if mode == "accu" else ())
-    log(f"[large tiles] mode={mode} p,q,r={p},{q},{r} s={s}")
+    want = ("d", "b", "Ap", "Bp", "At", "Bt", "R", "X") + (("P",) if raw_p else ()) + \
+        (("rho", "gamma", "Abar", "Bbar") if mode == "accu" else ())
+    log(f"[large tiles] mode={mode} raw_p={raw_p} p,q,r={p},{q},{r} s={s}")
     out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=want)
     torch.cuda.synchronize()
     rows = np.array(sorted(set(sample_indices(p, 10, 3).tolist()) | {1535, 1536, 1790, 1799}))
