@@ -86,7 +86,18 @@ def cpu_baseline(A, B, s, mode, rows, cols):
                   f"(scalings of the sampled rows/columns, their residues, s products, CRT, inverse scaling)",
         "seconds": dt,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def native_fp64_context(Ad, Bd, n, reps=10):
@@ -309,6 +320,10 @@ def main():
     stages = {
         "scaling_ms": st[0], "residues_ms": st[1], "gemm_ms": st[2], "crt_ms": st[3],
         "preprocess_fraction": (st[0] + st[1]) / total_stage,
+        # preprocess = scaling + residues against the HBM roof (accu's bound INT8 GEMM is
+        # counted in its time but not in its bytes, so its fraction is a lower bound)
+        "preprocess_ms": st[0] + st[1],
+        "preprocess_frac_hbm": (sb + rb) / ((st[0] + st[1]) * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "residues_GBs": rb / (st[1] * 1e-3) / 1e9,
         "residues_frac_hbm": rb / (st[1] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "scaling_GBs": sb / (st[0] * 1e-3) / 1e9,
