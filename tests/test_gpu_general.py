@@ -104,6 +104,36 @@ def test_k_blocked_inner_dimension(oz, mode):
     log("[kblock] ok")
 
 
+def test_k_blocked_on_large_grid(oz):
+    """q = 131372 (two K-blocks) with p = r = 1536, s = 15: 540 tiles of 256 x 256, so the first
+    K-block runs in the large-grid 16x16x64 kernel and the second accumulates its residues in
+    the K-block epilogue; sampled entries of R_t, X and C against the oracle."""
+    import torch
+    p, q, r, s = 1536, 131372, 1536, 15
+    A = generate(p, q, 0.5, 73)
+    B = generate(q, r, 0.5, 74)
+    log(f"[kblock large] p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, "fast", want=("d", "b", "R", "X"))
+    torch.cuda.synchronize()
+    rows = np.array([0, 255, 256, 777, 1279, 1535])
+    cols = np.array([1, 254, 511, 512, 1024, 1534])
+    ref = oracle.ozaki2_sample(A, B, s, "fast", rows, cols)
+    assert_equal(out["d"][rows].cpu().numpy(), ref["d"].astype(np.int32), "d")
+    assert_equal(out["b"][cols].cpu().numpy(), ref["b"].astype(np.int32), "b")
+    rows_t = torch.as_tensor(rows, device="cuda")
+    cols_t = torch.as_tensor(cols, device="cuda")
+    rt = out["R"][:, cols_t][:, :, rows_t].cpu().numpy()
+    for t in range(s):
+        assert_equal(rt[t], ref["R"][t].T.astype(np.uint8), f"R_t t={t}")
+    xg = out["X"][cols_t][:, rows_t].cpu().numpy()
+    for jj in range(len(cols)):
+        for ii in range(len(rows)):
+            assert x_limbs_to_int(xg[jj, ii]) == int(ref["X"][ii, jj]), f"X[{rows[ii]},{cols[jj]}]"
+    c = out["C"][rows_t][:, cols_t].cpu().numpy()
+    assert_chat_close(c, ref["C"], chat_tolerance(A, B, rows, cols), "C")
+    log("[kblock large] ok")
+
+
 def test_p_dump_refused_when_k_blocked(oz):
     import torch
     p, q, r = 8, oz.OZ2_MAX_Q_P_DUMP + 1, 8
