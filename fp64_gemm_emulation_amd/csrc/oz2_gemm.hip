@@ -3,6 +3,10 @@
 // R_t = P_t mod m_t fused into the epilogue ("Profiling Ozaki II: The Cost Behind Fast
 // INT8 GEMMs", Part I section 1: yellow GEMMs and blue output reduction), and the accu
 // bound product whose epilogue keeps only row / column maxima (same page, section 2).
+// Two kernels: gemm_w8_kernel (8 waves of v_mfma_i32_16x16x64_i8, two per SIMD) for grids
+// of at least two 256 x 256 tiles per CU, and gemm_i8_kernel (one wave of
+// v_mfma_i32_32x32x32_i8 per SIMD, 256 x 256 or 128 x 128 tiles) for smaller grids, the
+// later K-blocks of long inner dimensions and the raw P_t validation dump.
 //
 // Exactness: |A_t|, |B_t| <= 128, so every product is at most 2^14 and every partial sum
 // of a length-q dot product stays below q 2^14 < 2^31 for q < 2^17, in any order
