@@ -695,8 +695,10 @@ static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, h
   return hipSuccess;
 }
 
-// 256 x 256 tiles unless that grid gives fewer than two workgroups per CU, where the
-// exposed per-tile prologue / epilogue and the partly empty last round dominate.
+// 256 x 256 tiles (gemm_w8_kernel for the mod and bound epilogues of a whole launch,
+// gemm_i8_kernel for the raw P_t dump and the later K-blocks) unless that grid gives fewer
+// than two workgroups per CU, where the exposed per-tile prologue / epilogue and the
+// partly empty last round dominate and the 128 x 128-tile gemm_i8_kernel runs.
 hipError_t launch_gemm(const Work& w, int epi, const DumpPtrs& dump, hipStream_t st) {
   const long planes = epi == kEpiBound ? 1 : w.s;
   const long big_tiles = static_cast<long>(w.p_pad / 256) * (w.r_pad / 256) * planes;
