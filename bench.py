@@ -73,8 +73,9 @@ def cpu_baseline(A, B, s, mode, rows, cols):
     except Exception:  # pragma: no cover
         blas_threads = 1
     rows, cols = min(rows, A.shape[0]), min(cols, B.shape[1])
+    stage_s = {}
     t0 = time.perf_counter()
-    oracle.ozaki2_sample(A, B, s, mode, np.arange(rows), np.arange(cols))
+    oracle.ozaki2_sample(A, B, s, mode, np.arange(rows), np.arange(cols), timings=stage_s)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * A.shape[1] * cols
     return {
@@ -85,6 +86,7 @@ def cpu_baseline(A, B, s, mode, rows, cols):
         "sample": f"C[0:{rows}, 0:{cols}] of the {A.shape[0]}x{A.shape[1]}x{B.shape[1]} workload "
                   f"(scalings of the sampled rows/columns, their residues, s products, CRT, inverse scaling)",
         "seconds": dt,
+        "stage_seconds": stage_s,
         "host_cpus": len(os.sched_getaffinity(0)),
         "cpu_model": cpu_model(),
     }

@@ -60,6 +60,8 @@ from __future__ import annotations
 import math
 from fractions import Fraction
 
+import time
+
 import numpy as np
 
 __all__ = [
@@ -420,13 +422,19 @@ def ozaki2(A: np.ndarray, B: np.ndarray, s: int, mode: str = "fast") -> dict:
     return out
 
 
-def ozaki2_sample(A, B, s: int, mode: str, rows, cols) -> dict:
+def ozaki2_sample(A, B, s: int, mode: str, rows, cols, timings: dict | None = None) -> dict:
     """The same quantities restricted to output rows ``rows`` and columns ``cols``.
 
     Scaling exponents still see whole rows of A / columns of B (fast) or the
     whole bound product (accu), so the sampled entries equal those of a full
-    run.  At, Ap are len(rows) x q; Bt, Bp are q x len(cols).
+    run.  At, Ap are len(rows) x q; Bt, Bp are q x len(cols).  When ``timings``
+    is a dict it receives the wall seconds of each stage (scaling, residues,
+    gemm = products and output residues, crt = reconstruction and inverse
+    scaling); the computation is the same either way.
     """
+    clock = time.perf_counter
+    t_start = clock()
+    spent = {"scaling": 0.0, "residues": 0.0, "gemm": 0.0, "crt": 0.0}
     A = np.asarray(A, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
     rows = np.asarray(rows, dtype=np.int64)
@@ -457,19 +465,29 @@ def ozaki2_sample(A, B, s: int, mode: str, rows, cols) -> dict:
                    e=[e[i] for i in rows], f=[f[j] for j in cols])
     else:
         raise ValueError(f"mode must be 'fast' or 'accu', got {mode!r}")
+    t0 = clock()
+    spent["scaling"] = t0 - t_start
     ap = scale_truncate(a_rows, d)
     bp = scale_truncate(b_cols.T, b).T
     at, bt, pt, rt = [], [], [], []
     for m in mods:
         a_m = centered_residue(ap, m)
         b_m = centered_residue(bp, m)
+        t2 = clock()
         p_m = residue_product(a_m, b_m)
         at.append(a_m)
         bt.append(b_m)
         pt.append(p_m)
         rt.append(output_residue(p_m, m))
+        spent["gemm"] += clock() - t2
+    t3 = clock()
     x = crt(rt, s) if rt[0].size else np.zeros(rt[0].shape, dtype=object)
     c = inverse_scale(x, d, b)
+    spent["crt"] = clock() - t3
+    # scaled truncation and residues: everything between the scalings and the CRT but the products
+    spent["residues"] = (t3 - t0) - spent["gemm"]
+    if timings is not None:
+        timings.update(spent)
     out.update(d=d, b=b, Ap=ap, Bp=bp, At=at, Bt=bt, P=pt, R=rt, X=x, C=c, moduli=mods,
                rows=rows, cols=cols)
     return out
