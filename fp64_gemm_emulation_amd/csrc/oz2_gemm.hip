@@ -5,8 +5,8 @@
 // bound product whose epilogue keeps only row / column maxima (same page, section 2).
 // Two kernels: gemm_w8_kernel (8 waves of v_mfma_i32_16x16x64_i8, two per SIMD) for grids
 // of at least two 256 x 256 tiles per CU, and gemm_i8_kernel (one wave of
-// v_mfma_i32_32x32x32_i8 per SIMD, 256 x 256 or 128 x 128 tiles) for smaller grids, the
-// later K-blocks of long inner dimensions and the raw P_t validation dump.
+// v_mfma_i32_32x32x32_i8 per SIMD, 256 x 256 or 128 x 128 tiles) for smaller grids and
+// the raw P_t validation dump.
 //
 // Exactness: |A_t|, |B_t| <= 128, so every product is at most 2^14 and every partial sum
 // of a length-q dot product stays below q 2^14 < 2^31 for q < 2^17, in any order
@@ -162,6 +162,18 @@ __device__ __forceinline__ uint32_t residue_word4(const v4i& a, const ModRed& mr
   const uint32_t r01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
   const uint32_t r23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
   return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+}
+
+// Byte-wise (a + b) mod m of two words of residues in [0, m), m <= 256.
+__device__ __forceinline__ uint32_t add_mod_bytes(uint32_t a, uint32_t b, int m) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int x = static_cast<int>((a >> (8 * k)) & 0xFFu) + static_cast<int>((b >> (8 * k)) & 0xFFu);
+    x -= x >= m ? m : 0;
+    out |= static_cast<uint32_t>(x) << (8 * k);
+  }
+  return out;
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Give
@@ -472,15 +484,16 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
 // same for A and B, so the K positions one MFMA pairs up agree); the operand swizzle puts
 // the 16 rows of each chunk in distinct bank groups.  Accumulator register v of lane l of
 // a block holds row 4 (l / 16) + v, column l % 16.
-// EPI: kEpiMod (residues R_t) or kEpiBound (the accu bound product: row and column maxima
-// of the single plane, accumulators from 0).
+// EPI: kEpiMod (residues R_t), kEpiModAcc (a later K-block: R_t <- (P_block + R_t) mod m_t)
+// or kEpiBound (the accu bound product: row and column maxima of the single plane,
+// accumulators from 0).  Stages kt0 .. kt0 + nk - 1 of the inner dimension are multiplied.
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restrict__ at, const int8_t* __restrict__ bt,
-                                                         long a_plane, long b_plane, int K, int nk,
+                                                         long a_plane, long b_plane, int K, int kt0, int nk,
                                                          uint8_t* __restrict__ res, long r_plane, int ldr,
                                                          int* __restrict__ rho, int* __restrict__ gamma, int p, int r,
                                                          int tiles_m, int tiles_n) {
-  static_assert(EPI == kEpiMod || EPI == kEpiBound, "epilogues of the 8-wave GEMM");
+  static_assert(EPI == kEpiMod || EPI == kEpiModAcc || EPI == kEpiBound, "epilogues of the 8-wave GEMM");
   constexpr int BT = 256;
   constexpr int kSlice = BT * kBK;             // 16 KiB per operand per stage
   constexpr int kStageLds = 2 * kSlice;        // A then B
@@ -501,7 +514,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
   const int i0 = tile_i * BT;
   const int j0 = tile_j * BT;
   ModRed mr{0, 0, 0, 0.0f, 0.0f};
-  if constexpr (EPI == kEpiMod) {
+  if constexpr (EPI != kEpiBound) {
     mr = kModRed[t];
     asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
   }
@@ -510,7 +523,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
   // [4096 (w mod 4) + 1024 c, +1024) of it, lane l at byte 16 l.
   const int8_t* const gsrc = (wave < 4 ? at + t * a_plane + static_cast<long>(i0) * K
                                        : bt + t * b_plane + static_cast<long>(j0) * K) +
-                             (wave & 3) * 4096 + 16 * lane;
+                             static_cast<long>(kt0) * kTileBytes + (wave & 3) * 4096 + 16 * lane;
   int8_t* const gdst = smem + (wave >= 4 ? kSlice : 0) + (wave & 3) * 4096;
   auto copy1 = [&](int kbuf, int ksrc, int c) {
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(gsrc + static_cast<long>(ksrc) * kTileBytes + c * 1024),
@@ -639,7 +652,16 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
       const int y0 = x0w, y1 = x1w;
       x0w = x2w; x1w = x3w; x2w = y0; x3w = y1;
     }
-    *reinterpret_cast<v4i*>(rt + static_cast<long>(j0 + jl) * ldr + i0 + 16 * c) = v4i{x0w, x1w, x2w, x3w};
+    v4i* const dst = reinterpret_cast<v4i*>(rt + static_cast<long>(j0 + jl) * ldr + i0 + 16 * c);
+    if constexpr (EPI == kEpiModAcc) {
+      // add the previous K-blocks' residues byte by byte: both are below m, one subtraction
+      const v4i prev = *dst;
+      x0w = static_cast<int>(add_mod_bytes(static_cast<uint32_t>(x0w), static_cast<uint32_t>(prev[0]), mr.m));
+      x1w = static_cast<int>(add_mod_bytes(static_cast<uint32_t>(x1w), static_cast<uint32_t>(prev[1]), mr.m));
+      x2w = static_cast<int>(add_mod_bytes(static_cast<uint32_t>(x2w), static_cast<uint32_t>(prev[2]), mr.m));
+      x3w = static_cast<int>(add_mod_bytes(static_cast<uint32_t>(x3w), static_cast<uint32_t>(prev[3]), mr.m));
+    }
+    *dst = v4i{x0w, x1w, x2w, x3w};
   }
 }
 
@@ -665,7 +687,7 @@ static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, h
   if (epi == kEpiBound) {
     if constexpr (TB == 4)
       hipLaunchKernelGGL(gemm_w8_kernel<kEpiBound>, grid, dim3(512), 0, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad,
-                         nk, nullptr, 0L, w.p_pad, w.rho, w.gamma, w.p, w.r, tiles_m, tiles_n);
+                         0, nk, nullptr, 0L, w.p_pad, w.rho, w.gamma, w.p, w.r, tiles_m, tiles_n);
     else
       launch_tile<kEpiBound, TB>(grid, st, w.abar, w.bbar, a_plane, b_plane, w.q_pad, 0, nk, nullptr, 0L, w.p_pad,
                                  nullptr, w.p, w.r, w.rho, w.gamma, tiles_m, tiles_n);
@@ -677,15 +699,18 @@ static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, h
   if (epi == kEpiRawMod && nk > kBlockStages) return hipErrorInvalidValue;
   for (int kt0 = 0; kt0 == 0 || kt0 < nk; kt0 += kBlockStages) {
     const int nkb = nk - kt0 < kBlockStages ? nk - kt0 : kBlockStages;
-    if (kt0 > 0)
+    if (kt0 > 0 && TB == 4)
+      hipLaunchKernelGGL(gemm_w8_kernel<kEpiModAcc>, grid, dim3(512), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad, kt0,
+                         nkb, w.res, r_plane, w.p_pad, nullptr, nullptr, w.p, w.r, tiles_m, tiles_n);
+    else if (kt0 > 0)
       launch_tile<kEpiModAcc, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, kt0, nkb, w.res, r_plane, w.p_pad,
                                   nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
     else if (epi == kEpiRawMod)
       launch_tile<kEpiRawMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
                                   dump.pt, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
     else if constexpr (TB == 4)
-      hipLaunchKernelGGL(gemm_w8_kernel<kEpiMod>, grid, dim3(512), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad, nkb,
-                         w.res, r_plane, w.p_pad, nullptr, nullptr, w.p, w.r, tiles_m, tiles_n);
+      hipLaunchKernelGGL(gemm_w8_kernel<kEpiMod>, grid, dim3(512), 0, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0,
+                         nkb, w.res, r_plane, w.p_pad, nullptr, nullptr, w.p, w.r, tiles_m, tiles_n);
     else
       launch_tile<kEpiMod, TB>(grid, st, w.at, w.bt, a_plane, b_plane, w.q_pad, 0, nkb, w.res, r_plane, w.p_pad,
                                nullptr, w.p, w.r, nullptr, nullptr, tiles_m, tiles_n);
@@ -695,8 +720,8 @@ static hipError_t launch_gemm_tb(const Work& w, int epi, const DumpPtrs& dump, h
   return hipSuccess;
 }
 
-// 256 x 256 tiles (gemm_w8_kernel for the mod and bound epilogues of a whole launch,
-// gemm_i8_kernel for the raw P_t dump and the later K-blocks) unless that grid gives fewer
+// 256 x 256 tiles (gemm_w8_kernel for the mod, K-block and bound epilogues, gemm_i8_kernel
+// for the raw P_t dump) unless that grid gives fewer
 // than two workgroups per CU, where the exposed per-tile prologue / epilogue and the
 // partly empty last round dominate and the 128 x 128-tile gemm_i8_kernel runs.
 hipError_t launch_gemm(const Work& w, int epi, const DumpPtrs& dump, hipStream_t st) {
