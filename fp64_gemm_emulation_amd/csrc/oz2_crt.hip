@@ -2,55 +2,21 @@
 // ("Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part I section 1, red stage).
 //
 // X is computed exactly: with W_t = (M/m_t) ((M/m_t)^-1 mod m_t),
-//   X = sum_t R_t W_t - k M,   k = round(sum_t R_t W_t / M) = round(sum_t R_t c_t),
-//   c_t = ((M/m_t)^-1 mod m_t) / m_t.
+//   X = sum_t R_t W_t - k M,   k = round(sum_t R_t W_t / M).
 // W_t and M are split into 32-bit limbs held in doubles, so every limb sum is an exact
-// FP64 integer FMA chain (each partial sum < 20 * 2^8 * 2^32 < 2^53).  k is exact: the
-// scalings keep |X| <= 2^tau, so sum_t R_t c_t lies at least 0.014 (over all s = 2..20)
-// away from a half-integer, far above its FP64 rounding error (< 2^-35).  The limbs are
-// carried into a two's-complement multiword integer and converted to FP64 with one
-// round-to-nearest-even, then scaled by 2^-(d_i + b_j) with ldexp (exact unless the
-// result is subnormal).  The stored value is alpha Chat when beta = 0 (C is not read) and
-// fma(alpha, Chat, RN(beta C)) otherwise, so alpha = 1, beta = 0 stores Chat itself.
+// FP64 integer FMA chain (each partial sum < 20 * 2^8 * 2^32 < 2^53).  k comes from the two
+// top limb sums (the lower limbs cannot move the quotient across a half-integer: the
+// scalings keep |X| <= 2^tau).  The limbs are carried into [0, 2^32) with floor, which
+// makes them the two's-complement words of X, then rounded to FP64 with one
+// round-to-nearest-even and scaled by 2^-(d_i + b_j) with ldexp (exact unless the result is
+// subnormal); oz2_crt_round.hpp holds that step and why one FMA rounding is enough.  The
+// stored value is alpha Chat when beta = 0 (C is not read) and fma(alpha, Chat, RN(beta C))
+// otherwise, so alpha = 1, beta = 0 stores Chat itself.
 #include "oz2_common.hpp"
 #include "oz2_internal.hpp"
+#include "oz2_crt_round.hpp"
 
 namespace oz2 {
-
-// Round the magnitude held in words w[0..L-1] (little-endian) to a double with exponent
-// offset `scale`: returns RN(w) * 2^scale.
-template <int L>
-__device__ __forceinline__ double words_to_double(const uint32_t (&w)[L], int scale) {
-  int h = 0;
-#pragma unroll
-  for (int k = 1; k < L; ++k)
-    if (w[k] != 0) h = k;
-  uint32_t w2 = 0, w1 = 0, w0 = 0;
-  bool sticky = false;
-#pragma unroll
-  for (int k = 0; k < L; ++k) {
-    if (k == h) w2 = w[k];
-    if (k == h - 1) w1 = w[k];
-    if (k == h - 2) w0 = w[k];
-    if (k < h - 2) sticky |= w[k] != 0;
-  }
-  if (w2 == 0) return 0.0;  // then h == 0 and the value is 0
-  const int lz = __clz(static_cast<int>(w2));
-  uint64_t top = (static_cast<uint64_t>(w2) << 32) | w1;
-  if (lz > 0) {
-    top = (top << lz) | (static_cast<uint64_t>(w0) >> (32 - lz));
-    sticky |= (w0 << lz) != 0;
-  } else {
-    sticky |= w0 != 0;
-  }
-  // bit 63 of top is the leading one; keep 53 bits and round to nearest even
-  uint64_t mant = top >> 11;
-  const bool rbit = ((top >> 10) & 1ull) != 0;
-  sticky |= (top & 0x3FFull) != 0;
-  if (rbit && (sticky || (mant & 1ull))) mant += 1;  // may reach 2^53: still exact
-  const int e2 = 32 * h + 31 - lz - 52;
-  return ldexp(static_cast<double>(mant), e2 + scale);
-}
 
 // Thread: kRowsPerThread consecutive rows i0.. of one column j; it reads kRowsPerThread
 // bytes of each residue plane with one load (so each plane read of a wave covers
@@ -86,52 +52,37 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ re
       rw[t][0] = *reinterpret_cast<const uint32_t*>(src + t * r_plane);
     }
   }
+  // plane by plane, so each limb constant is loaded once for the thread's outputs
+  double acc[kRowsPerThread][L];
+#pragma unroll
+  for (int v = 0; v < kRowsPerThread; ++v)
+#pragma unroll
+    for (int k = 0; k < L; ++k) acc[v][k] = 0.0;
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    double rt[kRowsPerThread];
+#pragma unroll
+    for (int v = 0; v < kRowsPerThread; ++v) rt[v] = static_cast<double>((rw[t][v >> 2] >> (8 * (v & 3))) & 0xFFu);
+#pragma unroll
+    for (int v = 0; v < kRowsPerThread; ++v) crt_accumulate<S>(acc[v], rt[v], t);
+  }
   const int bj = b[j];
   double out[kRowsPerThread];
 #pragma unroll
   for (int v = 0; v < kRowsPerThread; ++v) {
     const int i = min(i0 + v, p - 1);  // rows past p (last group only) are computed, not stored
-    double acc[L];
-#pragma unroll
-    for (int k = 0; k < L; ++k) acc[k] = 0.0;
-    double f = 0.0;
-#pragma unroll
-    for (int t = 0; t < S; ++t) {
-      const double rt = static_cast<double>((rw[t][v >> 2] >> (8 * (v & 3))) & 0xFFu);
-      f = fma(rt, kCrt<S>.c[t], f);
-#pragma unroll
-      for (int k = 0; k < L; ++k) acc[k] = fma(rt, kCrt<S>.w[t][k], acc[k]);
-    }
-    const double kq = rint(f);
-#pragma unroll
-    for (int k = 0; k < L; ++k) acc[k] = fma(-kq, kCrt<S>.m[k], acc[k]);
-    // carry into 32-bit words (two's complement, top word signed)
-    uint32_t wd[L];
-#pragma unroll
-    for (int k = 0; k < L - 1; ++k) {
-      const double cy = floor(acc[k] * 0x1p-32);
-      wd[k] = static_cast<uint32_t>(fma(-cy, 0x1p32, acc[k]));
-      acc[k + 1] += cy;
-    }
-    const int top = static_cast<int>(acc[L - 1]);
-    wd[L - 1] = static_cast<uint32_t>(top);
+    crt_reduce<S>(acc[v]);
+    crt_normalize<L>(acc[v]);
     if (DUMPX && i0 + v < p) {
+      // the normalised limbs are the two's-complement words of X (top word signed)
+      const int top = static_cast<int>(acc[v][L - 1]);
       uint32_t* xd = x_dump + (static_cast<long>(j) * p + i) * 5;
 #pragma unroll
-      for (int k = 0; k < 5; ++k) xd[k] = k < L ? wd[k] : (top < 0 ? 0xFFFFFFFFu : 0u);
+      for (int k = 0; k < 5; ++k)
+        xd[k] = k < L - 1 ? static_cast<uint32_t>(acc[v][k])
+                          : (k == L - 1 ? static_cast<uint32_t>(top) : (top < 0 ? 0xFFFFFFFFu : 0u));
     }
-    const bool neg = top < 0;
-    if (neg) {  // magnitude = ~X + 1
-      uint32_t carry = 1;
-#pragma unroll
-      for (int k = 0; k < L; ++k) {
-        const uint32_t nv = ~wd[k] + carry;
-        carry = (carry != 0 && nv == 0) ? 1u : 0u;
-        wd[k] = nv;
-      }
-    }
-    const double mag = words_to_double<L>(wd, -(d[i] + bj));
-    out[v] = neg ? -mag : mag;
+    out[v] = crt_round<L, CrtTable<S>::kTopExp>(acc[v], -(d[i] + bj));
   }
   double* dst = C + i0 + static_cast<long>(j) * ldc;
   if (beta != 0.0) {

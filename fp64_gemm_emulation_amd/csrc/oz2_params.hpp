@@ -184,36 +184,50 @@ constexpr int limb_coef(int t, int k) {
 }
 
 // ---------------------------------------------------------------------------
-// CRT constants: X = sum_t R_t W_t - k M, W_t = (M / m_t) * ((M / m_t)^-1 mod m_t),
-// k = rint(sum_t R_t c_t), c_t = W_t / M = ((M / m_t)^-1 mod m_t) / m_t.
+// CRT constants: X = sum_t R_t W_t - k M, W_t = (M / m_t) * ((M / m_t)^-1 mod m_t).
 // W_t and M are held as 32-bit limbs stored in doubles so the weighted sums are exact
-// FP64 integer FMAs (every partial sum stays below 20 * 2^8 * 2^32 < 2^53).
+// FP64 integer FMAs (every partial sum stays below 20 * 2^8 * 2^32 < 2^53).  k is the
+// nearest integer to sum_t R_t W_t / M, estimated from the two top limb sums alone:
+// k = rint(acc[L-1] q1 + acc[L-2] q0) with q1 = 2^(32 (L-1)) / M, q0 = 2^(32 (L-2)) / M.
+// The limbs left out add less than 20 * 255 * 2^(32 (L-2)) * (1 + 2^-31) / M < 2^-19
+// (M > 2^(32 (L-1))), and the scalings keep |X| <= 2^tau, which puts the exact quotient at
+// least 0.014 from a half-integer for every s: the estimate rounds to k.
 // ---------------------------------------------------------------------------
 constexpr int crt_limbs(int S) { return (big_bitlen(modulus_product(S)) + 31) / 32; }
 
 template <int S>
 struct CrtTable {
   static constexpr int L = crt_limbs(S);
+  // |floor(X / 2^(32 (L-1)))| <= 2^kTopExp for |X| <= 2^tau
+  static constexpr int kTopExp = tau_of(S) - 32 * (L - 1);
   double w[S][L];
-  double c[S];
   double m[L];
+  double q1, q0;
 };
 
 template <int S>
 constexpr CrtTable<S> make_crt() {
   CrtTable<S> tab{};
+  constexpr int L = CrtTable<S>::L;
   Big M = modulus_product(S);
-  for (int k = 0; k < CrtTable<S>::L; ++k) tab.m[k] = static_cast<double>(M.w[k]);
+  double md = 0.0;
+  for (int k = kBigLimbs - 1; k >= 0; --k) md = md * 0x1p32 + static_cast<double>(M.w[k]);
+  for (int k = 0; k < L; ++k) tab.m[k] = static_cast<double>(M.w[k]);
   for (int t = 0; t < S; ++t) {
     uint32_t mt = static_cast<uint32_t>(modulus(t));
     Big rest = product_except(S, t);
     uint32_t inv = inv_mod(big_mod_small(rest, mt), mt);
     Big w = big_mul_small(rest, inv);
-    for (int k = 0; k < CrtTable<S>::L; ++k) tab.w[t][k] = static_cast<double>(w.w[k]);
-    tab.c[t] = static_cast<double>(inv) / static_cast<double>(mt);
+    for (int k = 0; k < L; ++k) tab.w[t][k] = static_cast<double>(w.w[k]);
   }
+  double p1 = 1.0;
+  for (int k = 0; k < 32 * (L - 1); ++k) p1 *= 2.0;
+  tab.q1 = p1 / md;
+  tab.q0 = L >= 2 ? tab.q1 * 0x1p-32 : 0.0;
   return tab;
 }
+
+static_assert(CrtTable<kMaxS>::kTopExp <= 30 && CrtTable<kMinS>::L == 1, "top limb fits int32");
 
 template <int S>
 inline constexpr CrtTable<S> kCrt = make_crt<S>();

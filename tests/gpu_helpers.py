@@ -43,6 +43,14 @@ def assert_chat_close(c_gpu, c_ref, tol, what=""):
     assert not bad.any(), f"{what}: {bad.sum()} entries out of tolerance, max excess {np.max(diff - tol)}"
 
 
+def assert_correctly_rounded(c_gpu, c_ref, what=""):
+    """C is RN(X) 2^-(d_i + b_j) on the GPU and RN(X 2^-(d_i + b_j)) in the oracle: the same
+    double wherever the result is normal (below that, the scaling may round a second time)."""
+    normal = (np.abs(c_ref) >= 2.0 ** -1021) | (c_ref == 0)
+    bad = normal & (c_gpu != c_ref)
+    assert not bad.any(), f"{what}: {bad.sum()} normal entries differ from the correctly rounded value"
+
+
 def compare_full(out, ref, A, B, s, mode):
     """Every intermediate of a full run, bit-exact; C within the benchmark spec's tolerance."""
     p, q = A.shape
@@ -81,6 +89,7 @@ def compare_full(out, ref, A, B, s, mode):
     c = out["C"].cpu().numpy()
     tol = chat_tolerance(A, B, np.arange(p), np.arange(r))
     assert_chat_close(c, ref["C"], tol, "C")
+    assert_correctly_rounded(c, ref["C"], "C")
     return int(np.sum(c != ref["C"]))
 
 
@@ -120,6 +129,7 @@ def compare_sampled(out, ref, A, B, s, mode, rows, cols):
     c = out["C"][rows_t][:, cols_t].cpu().numpy()
     tol = chat_tolerance(A, B, rows, cols)
     assert_chat_close(c, ref["C"], tol, "C")
+    assert_correctly_rounded(c, ref["C"], "C")
     return int(np.sum(c != ref["C"]))
 
 
