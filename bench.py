@@ -92,6 +92,20 @@ def cpu_baseline(A, B, s, mode, rows, cols):
     }
 
 
+def host_fp64_matmul_context(A, B, m=2048, reps=3):
+    """Host FP64 BLAS (numpy) on the leading m x m blocks of the operands, for context."""
+    import numpy as np
+    m = min(m, A.shape[0], A.shape[1], B.shape[1])
+    a = np.ascontiguousarray(A[:m, :m])
+    b = np.ascontiguousarray(B[:m, :m])
+    best = float("inf")
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        np.matmul(a, b)
+        best = min(best, time.perf_counter() - t0)
+    return {"host_fp64_matmul_tflops": 2.0 * m ** 3 / best / 1e12, "host_fp64_matmul_shape": m}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -375,6 +389,8 @@ def main():
         result["context"] = ctx
     if not args.no_cpu_baseline and not args.zero_inputs:
         result["cpu_baseline"] = cpu_baseline(A, B, s, w.mode, args.cpu_rows, args.cpu_cols)
+        if "context" in result:
+            result["context"].update(host_fp64_matmul_context(A, B))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
