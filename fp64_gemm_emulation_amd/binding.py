@@ -147,10 +147,21 @@ def empty_colmajor(rows, cols, device="cuda", dtype=None):
     return torch.empty((cols, rows), dtype=dtype or torch.float64, device=device).t()
 
 
-def _stream_ptr(stream):
+def _stream_ptr(stream, device):
     import torch
-    st = stream if stream is not None else torch.cuda.current_stream()
+    st = stream if stream is not None else torch.cuda.current_stream(device)
     return st.cuda_stream
+
+
+def _on_device(*tensors):
+    """The operands' common device, made current for the call (the library works on the
+    current device)."""
+    import torch
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError("all operands must be on the same device")
+    return torch.cuda.device(dev)
 
 
 def dgemm(A, B, s: int = 14, mode: str = "fast", out=None, stream=None):
@@ -160,8 +171,11 @@ def dgemm(A, B, s: int = 14, mode: str = "fast", out=None, stream=None):
     if q != q2:
         raise ValueError("inner dimensions differ")
     C = out if out is not None else empty_colmajor(p, r, device=A.device)
-    rc = ozaki2_dgemm(p, q, r, A.data_ptr(), _colmajor_ld(A, "A"), B.data_ptr(), _colmajor_ld(B, "B"),
-                      C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode], _stream_ptr(stream))
+    if tuple(C.shape) != (p, r):
+        raise ValueError("out has the wrong shape")
+    with _on_device(A, B, C):
+        rc = ozaki2_dgemm(p, q, r, A.data_ptr(), _colmajor_ld(A, "A"), B.data_ptr(), _colmajor_ld(B, "B"),
+                          C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode], _stream_ptr(stream, A.device))
     if rc != OZ2_OK:
         raise Oz2Error(rc, "ozaki2_dgemm")
     return C
@@ -181,9 +195,11 @@ def dgemm_ex(A, B, transa: bool = False, transb: bool = False, alpha: float = 1.
         C = empty_colmajor(p, r, device=A.device)
     if tuple(C.shape) != (p, r):
         raise ValueError("C has the wrong shape")
-    rc = ozaki2_dgemm_ex(OZ2_OP_T if transa else OZ2_OP_N, OZ2_OP_T if transb else OZ2_OP_N, p, q, r, float(alpha),
-                         A.data_ptr(), _colmajor_ld(A, "A"), B.data_ptr(), _colmajor_ld(B, "B"), float(beta),
-                         C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode], _stream_ptr(stream))
+    with _on_device(A, B, C):
+        rc = ozaki2_dgemm_ex(OZ2_OP_T if transa else OZ2_OP_N, OZ2_OP_T if transb else OZ2_OP_N, p, q, r,
+                             float(alpha), A.data_ptr(), _colmajor_ld(A, "A"), B.data_ptr(), _colmajor_ld(B, "B"),
+                             float(beta), C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode],
+                             _stream_ptr(stream, A.device))
     if rc != OZ2_OK:
         raise Oz2Error(rc, "ozaki2_dgemm_ex")
     return C
@@ -212,8 +228,9 @@ def dgemm_debug(A, B, s: int = 14, mode: str = "fast", want=DUMP_FIELDS, stream=
     }
     bufs = {k: torch.zeros(*shapes[k][0], dtype=shapes[k][1], device=dev) for k in want}
     dump = OZ2Dump(**{k: (bufs[k].data_ptr() if bufs[k].numel() else None) for k in want})
-    rc = ozaki2_dgemm_debug(p, q, r, A.data_ptr(), _colmajor_ld(A, "A"), B.data_ptr(), _colmajor_ld(B, "B"),
-                            C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode], _stream_ptr(stream), dump)
+    with _on_device(A, B, C):
+        rc = ozaki2_dgemm_debug(p, q, r, A.data_ptr(), _colmajor_ld(A, "A"), B.data_ptr(), _colmajor_ld(B, "B"),
+                                C.data_ptr(), _colmajor_ld(C, "C"), s, MODES[mode], _stream_ptr(stream, dev), dump)
     if rc != OZ2_OK:
         raise Oz2Error(rc, "ozaki2_dgemm_debug")
     if "Ap" in bufs:

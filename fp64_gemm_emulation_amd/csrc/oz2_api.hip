@@ -167,9 +167,13 @@ int validate(const Call& c, const oz2_dump_t* dump) {
 // ---------------------------------------------------------------------------
 // Library state: workspace and timing
 // ---------------------------------------------------------------------------
+struct Owned {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
 struct State {
-  void* owned = nullptr;
-  size_t owned_bytes = 0;
+  std::vector<Owned> owned;  // library-owned workspace, one per device ordinal
   void* user = nullptr;
   size_t user_bytes = 0;
   // timing
@@ -190,21 +194,26 @@ int acquire_workspace(size_t need, char** base) {
     *base = static_cast<char*>(g.user);
     return OZ2_OK;
   }
-  if (g.owned_bytes < need) {
-    if (g.owned != nullptr) {
+  // the buffer of the device current at this call (each device gets its own)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return OZ2_ERR_HIP;
+  if (g.owned.size() <= static_cast<size_t>(dev)) g.owned.resize(static_cast<size_t>(dev) + 1);
+  Owned& o = g.owned[static_cast<size_t>(dev)];
+  if (o.bytes < need) {
+    if (o.ptr != nullptr) {
       if (hipDeviceSynchronize() != hipSuccess) return OZ2_ERR_HIP;
-      (void)hipFree(g.owned);
-      g.owned = nullptr;
-      g.owned_bytes = 0;
+      (void)hipFree(o.ptr);
+      o.ptr = nullptr;
+      o.bytes = 0;
     }
-    if (hipMalloc(&g.owned, need) != hipSuccess) {
-      g.owned = nullptr;
+    if (hipMalloc(&o.ptr, need) != hipSuccess) {
+      o.ptr = nullptr;
       (void)hipGetLastError();
       return OZ2_ERR_WORKSPACE;
     }
-    g.owned_bytes = need;
+    o.bytes = need;
   }
-  *base = static_cast<char*>(g.owned);
+  *base = static_cast<char*>(o.ptr);
   return OZ2_OK;
 }
 
@@ -336,14 +345,20 @@ int ozaki2_set_workspace(void* dev_ptr, size_t bytes) {
 
 int ozaki2_release(void) {
   int rc = OZ2_OK;
-  if (g.owned != nullptr || !g.events.empty()) {
-    if (hipDeviceSynchronize() != hipSuccess) rc = OZ2_ERR_HIP;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) rc = OZ2_ERR_HIP;
+  if (!g.events.empty() && hipDeviceSynchronize() != hipSuccess) rc = OZ2_ERR_HIP;
+  for (size_t dev = 0; dev < g.owned.size(); ++dev) {
+    Owned& o = g.owned[dev];
+    if (o.ptr == nullptr) continue;
+    // synchronize and free on the device that owns the buffer
+    if (hipSetDevice(static_cast<int>(dev)) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipFree(o.ptr) != hipSuccess)
+      rc = OZ2_ERR_HIP;
+    o.ptr = nullptr;
+    o.bytes = 0;
   }
-  if (g.owned != nullptr) {
-    if (hipFree(g.owned) != hipSuccess) rc = OZ2_ERR_HIP;
-    g.owned = nullptr;
-    g.owned_bytes = 0;
-  }
+  if (!g.owned.empty() && hipSetDevice(cur) != hipSuccess) rc = OZ2_ERR_HIP;
   for (hipEvent_t e : g.events) (void)hipEventDestroy(e);
   g.events.clear();
   g.timing = false;

@@ -80,8 +80,9 @@ enum {
  *   p, q, r : sizes (>= 0; p == 0 or r == 0 is a no-op; q == 0 writes C = 0).
  *   s       : number of moduli, OZ2_MIN_S..OZ2_MAX_S.
  *   mode    : OZ2_FAST or OZ2_ACCU.
- * Uses the workspace set by ozaki2_set_workspace, else a library-owned device buffer
- * that is allocated (or grown) on first need and kept until ozaki2_release().
+ * Uses the workspace set by ozaki2_set_workspace, else a library-owned buffer on the
+ * current device (one per device) that is allocated (or grown) on first need and kept
+ * until ozaki2_release(); growing it synchronizes the current device.
  * Returns OZ2_OK, OZ2_ERR_ARG, OZ2_ERR_UNSUPPORTED, OZ2_ERR_WORKSPACE or OZ2_ERR_HIP.
  */
 int ozaki2_dgemm(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
@@ -112,12 +113,14 @@ int ozaki2_dgemm_ex(int transa, int transb, int p, int q, int r, double alpha, c
  * (0 if the arguments are invalid or describe no work). */
 size_t ozaki2_workspace_size(int p, int q, int r, int s, int mode);
 
-/* Use a caller-owned device buffer (256-byte aligned, `bytes` long) as the workspace.
- * dev_ptr == NULL reverts to the library-owned buffer.  The caller keeps ownership and
- * must keep the buffer alive while calls using it are in flight. */
+/* Use a caller-owned device buffer (256-byte aligned, `bytes` long) as the workspace of
+ * every following call, whichever device is current (it must be memory of the device the
+ * calls run on).  dev_ptr == NULL reverts to the library-owned buffers.  The caller keeps
+ * ownership and must keep the buffer alive while calls using it are in flight. */
 int ozaki2_set_workspace(void* dev_ptr, size_t bytes);
 
-/* Free the library-owned workspace and timing events (synchronizes the device). */
+/* Free the library-owned workspaces (synchronizing each device that holds one) and the
+ * timing events (synchronizing the current device). */
 int ozaki2_release(void);
 
 /*

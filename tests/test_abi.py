@@ -141,3 +141,21 @@ def test_calibration_library_exports_entry_point(lib):
     fn.restype = ctypes.c_int
     assert fn(None, 1, 1, None, None) == 1
     assert fn(ctypes.c_void_p(16), 0, 1, ctypes.c_void_p(16), None) == 1
+
+
+def test_tensor_wrappers_reject_bad_operands_before_the_library(lib):
+    """The torch conveniences check shapes, dtypes and devices on the host and raise
+    before any library call (nothing here touches a GPU)."""
+    import torch
+    a = torch.zeros(4, 3, dtype=torch.float64)
+    b = torch.zeros(3, 5, dtype=torch.float64)
+    with pytest.raises(ValueError, match="inner dimensions"):
+        lib.dgemm(a, torch.zeros(4, 5, dtype=torch.float64))
+    with pytest.raises(ValueError, match="wrong shape"):
+        lib.dgemm(a, b, out=torch.zeros(5, 4, dtype=torch.float64))
+    with pytest.raises(ValueError):          # host tensors are not device memory
+        lib.dgemm(a, b)
+    with pytest.raises(ValueError, match="beta != 0 needs C"):
+        lib.dgemm_ex(a, b, beta=1.0)
+    with pytest.raises(ValueError, match="wrong shape"):
+        lib.dgemm_ex(a, b, C=torch.zeros(4, 4, dtype=torch.float64))
