@@ -153,34 +153,37 @@ static_assert(tau_of(2) == 14 && tau_of(8) == 62 && tau_of(14) == 109 && tau_of(
               "tau = floor(log2(M/2 - 1))");
 
 // ---------------------------------------------------------------------------
-// Residue kernel: limb layout of |A'| and per-modulus constants
+// Residue kernel: digit layout of A' and per-modulus constants
 // ---------------------------------------------------------------------------
-// |A'| is split into a low limb of kLimb0 bits and NLHI limbs of kLimbHi bits.  For
-// an odd modulus m the reduced value z = L0 + sum_k c_k L_k (c_k the centered residue
-// of 2^(bit offset of limb k)) satisfies |z| < 2^22 + NLHI * 127 * 2^12 < 2^23, so
-// it is exact in FP32 and its nearest quotient by m can be taken in FP32.
-constexpr int kLimb0 = 22;
-constexpr int kLimbHi = 12;
+// A' = lo + 2^kLoBits H with lo in [0, 2^kLoBits) and H = floor(A' / 2^kLoBits) held as
+// balanced base-256 digits d_k in [-128, 127].  For an odd modulus m the reduced value
+// z = lo + sum_k d_k c_k (c_k the centered residue of 2^(kLoBits + 8 k), |c_k| <= 127)
+// satisfies |z| < 2^22 + 8 * 128 * 127 < 2^23, so it is exact in FP32 and its nearest
+// quotient by m can be taken in FP32.
+constexpr int kLoBits = 22;
 
 // Bit length bound of |A'|: fast keeps ||2^d_i A(i,:)||_2 <= 2^(tau/2); accu keeps
 // |A'| < 2^(floor(tau/2) + kQBits).
 constexpr int max_bits(int S, bool accu) { return accu ? tau_of(S) / 2 + kQBits : tau_of(S) / 2 + 1; }
 
-constexpr int nl_hi(int S, bool accu) {
-  int extra = max_bits(S, accu) - kLimb0;
-  return extra <= 0 ? 0 : (extra + kLimbHi - 1) / kLimbHi;
-}
-
-static_assert(nl_hi(kMaxS, true) <= 8, "|z| < 2^23 needs at most 8 high limbs");
+// Words of four digits that carry H: four balanced digits hold |H| < 2^31, eight |H| < 2^63.
+constexpr int digit_words(int S, bool accu) { return max_bits(S, accu) - kLoBits <= 30 ? 1 : 2; }
+static_assert(max_bits(kMaxS, true) - kLoBits <= 62, "two digit words hold H");
 
 constexpr int centered_small(uint32_t r, uint32_t m) {
   return (r > (m - 1) / 2) ? static_cast<int>(r) - static_cast<int>(m) : static_cast<int>(r);
 }
 
-// coefficient of high limb k (1-based) for modulus t: rho_m(2^(kLimb0 + kLimbHi (k-1)))
-constexpr int limb_coef(int t, int k) {
-  return centered_small(pow2_mod(kLimb0 + kLimbHi * (k - 1), static_cast<uint32_t>(modulus(t))),
-                        static_cast<uint32_t>(modulus(t)));
+// The four signed-byte coefficients rho_m(2^(kLoBits + 8 k)), k = 4 w .. 4 w + 3, of digit
+// word w for modulus index t, packed little-endian.
+constexpr int digit_coefs(int t, int w) {
+  uint32_t packed = 0;
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t m = static_cast<uint32_t>(modulus(t));
+    const int c = centered_small(pow2_mod(kLoBits + 8 * (4 * w + k), m), m);
+    packed |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * k);
+  }
+  return static_cast<int>(packed);
 }
 
 // ---------------------------------------------------------------------------

@@ -4,18 +4,20 @@
 // "Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part II section 8 identifies the
 // repeated per-modulus FP64 remainder chain as the preprocessing bottleneck and section
 // 10.1 proposes converting each scaled element to an integer once and reducing it with
-// fixed-divisor integer arithmetic.  This kernel goes further:
-//   * the scaled, truncated value is never formed in floating point: from the FP64
-//     fields (sign, 53-bit significand mu, exponent eta) |A'| = floor(mu 2^(eta + d)),
-//     exactly, for any magnitude (not only below 2^63);
-//   * |A'| is cut once into a 22-bit limb and NLHI 12-bit limbs, the sign is applied to
-//     the limbs, and per modulus one dot product with the compile-time centered residues
-//     of the limb weights gives z = A' (mod m) with |z| < 2^23 (v_mad_i32_i24);
-//   * z - m round(z/m) is the centered residue for odd m; round(z/m) comes from one FP32
-//     FMA that is exact at this size, and the final v_mad_i32_i24 lands the residue in
-//     the low byte (the extra multiple m 2^22 it carries is 0 mod 256);
-//   * m = 256 is the low byte of the signed low limb.
-// No FP64 arithmetic and no integer division run inside the modulus loop.
+// fixed-divisor integer arithmetic.  Here:
+//   * A' = trunc(2^d x) is formed once, exactly, in FP64 (any magnitude the scalings
+//     allow, not only below 2^63), and split with exact FP64 steps into a 22-bit low part
+//     lo and H = floor(A' / 2^22), which is written as eight balanced base-256 digits
+//     (signed bytes) in two words;
+//   * per odd modulus, one or two v_dot4_i32_i8 with the compile-time centered residues of
+//     the digit weights give z = lo + sum_k d_k rho_m(2^(22 + 8 k)) = A' (mod m),
+//     |z| < 2^23;
+//   * z - m round(z/m) is the centered residue; round(z/m) comes from one FP32 FMA that is
+//     exact at this size, and the final v_mad_i32_i24 lands the residue in the low byte
+//     (the extra multiple m 2^22 it carries is 0 mod 256);
+//   * m = 256 is the low byte of lo (A' in two's complement).
+// No FP64 arithmetic and no integer division run inside the modulus loop: five VALU
+// instructions per odd modulus and element.
 //
 // Output layout: planes A_t[t] (p_pad x q_pad) and B_t[t] (r_pad x q_pad, one row per
 // column of B) int8, tile-contiguous for the GEMM (operand_chunk_offset); each thread
@@ -33,48 +35,31 @@ struct ModConst {
   static constexpr float inv = 1.0f / static_cast<float>(modulus(T));
 };
 
-// Signed limbs of A' = trunc(2^scale x): l[0] = 22 low bits, l[k] = 12-bit limb at bit
-// 22 + 12 (k - 1); the sign of x is applied to every limb.  Also returns A' as an exact
+// A' = trunc(2^scale x) = lo + 2^22 H with lo in [0, 2^22) and H = floor(A' / 2^22) held
+// as eight balanced base-256 digits (signed bytes d_0..d_7, H = sum d_k 256^k) in w0, w1:
+// with C = 0x80...80, the bytes of H + C are d_k + 128, so those of (H + C) ^ C are d_k.
+// Exact for |H| < 2^62 (every s up to 20 in both modes).  Also returns A' as an exact
 // double when requested.
-template <int NLHI>
-__device__ __forceinline__ void scaled_limbs(double x, int scale, int (&l)[NLHI + 1], double* ap) {
-  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(x));
-  const bool neg = (bits >> 63) != 0;
-  const int be = static_cast<int>((bits >> 52) & 0x7FF);
-  uint64_t mu = bits & 0xFFFFFFFFFFFFFull;
-  if (be != 0) mu |= 1ull << 52;
-  if (be == 0x7FF) mu = 0;  // non-finite input: flagged in the scaling stage, treated as 0
-  const int sig = (be != 0 ? be - 1075 : -1074) + scale;
-  uint64_t lo, hi;
-  if (sig >= 0) {
-    const int sh = min(sig, 63);
-    lo = mu << sh;
-    hi = sh == 0 ? 0ull : mu >> (64 - sh);
-  } else {
-    const int sh = -sig;
-    lo = sh < 64 ? mu >> sh : 0ull;
-    hi = 0ull;
-  }
-  if (ap != nullptr) {
-    const double v = sig >= 0 ? ldexp(static_cast<double>(mu), sig) : static_cast<double>(lo);
-    *ap = neg ? -v : v;
-  }
-  // the sign is applied with a select so the compiler keeps the 24-bit range of each limb
-  const int l0 = static_cast<int>(lo & ((1ull << kLimb0) - 1));
-  l[0] = neg ? -l0 : l0;
-#pragma unroll
-  for (int k = 1; k <= NLHI; ++k) {
-    const int pos = kLimb0 + kLimbHi * (k - 1);
-    uint64_t f;
-    if (pos + kLimbHi <= 64)
-      f = lo >> pos;
-    else if (pos >= 64)
-      f = hi >> (pos - 64);
-    else
-      f = (lo >> pos) | (hi << (64 - pos));
-    const int lk = static_cast<int>(f & ((1ull << kLimbHi) - 1));
-    l[k] = neg ? -lk : lk;
-  }
+struct ScaledDigits {
+  int lo;
+  uint32_t w0, w1;
+};
+
+__device__ __forceinline__ ScaledDigits scaled_digits(double x, int scale, double* ap) {
+  // every step below is exact: A' is an integer below 2^84 with at most 53 significant
+  // bits, scalings by powers of two do not round, floor and the FMAs produce integers that
+  // fit (a value that underflows in ldexp is below 1 and truncates to 0 either way)
+  const double xf = __builtin_isfinite(x) ? x : 0.0;  // non-finite: flagged in the scaling stage
+  const double a = trunc(ldexp(xf, scale));            // A' = trunc(2^scale x)
+  if (ap != nullptr) *ap = a;
+  const double h = floor(a * 0x1p-22);                 // H = floor(A' / 2^22), |H| < 2^62
+  const int lo = static_cast<int>(fma(-h, 0x1p22, a));  // A' - 2^22 H in [0, 2^22)
+  const double hh = floor(h * 0x1p-32);                // |hh| < 2^30
+  const uint32_t hl = static_cast<uint32_t>(fma(-hh, 0x1p32, h));
+  const uint64_t hb = (static_cast<uint64_t>(static_cast<uint32_t>(static_cast<int>(hh))) << 32) | hl;
+  constexpr uint64_t kC = 0x8080808080808080ull;
+  const uint64_t dg = (hb + kC) ^ kC;
+  return ScaledDigits{lo, static_cast<uint32_t>(dg), static_cast<uint32_t>(dg >> 32)};
 }
 
 // a[23:0] * b[23:0] + c with signed 24-bit operands, as one full-rate v_mad_i32_i24
@@ -86,17 +71,38 @@ __device__ __forceinline__ int mad_i24(int a, int b, int c) {
   return d;
 }
 
-// Centered residue of the value held in signed limbs, for modulus index T, in the low
-// byte of the returned int (higher bits are not meaningful).
-template <int T, int NLHI>
-__device__ __forceinline__ int residue_byte(const int (&l)[NLHI + 1]) {
+// Digit coefficients of every modulus, in SGPRs: the empty asm makes them opaque to the
+// optimizer, so the dot products take them as scalar operands (the three-operand form,
+// which keeps lo) instead of as literals (the two-operand form, which would copy lo into
+// the accumulator before every product).
+struct DigitCoefs {
+  int c[kMaxS][2];
+};
+
+template <int S, int ND>
+__device__ __forceinline__ DigitCoefs load_coefs() {
+  DigitCoefs cf{};
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    cf.c[t][0] = digit_coefs(t, 0);
+    cf.c[t][1] = ND > 1 ? digit_coefs(t, 1) : 0;
+    asm volatile("" : "+s"(cf.c[t][0]));
+    if constexpr (ND > 1) asm volatile("" : "+s"(cf.c[t][1]));
+  }
+  return cf;
+}
+
+// Centered residue of A' for modulus index T, in the low byte of the returned int (higher
+// bits are not meaningful).  ND: 1 or 2 digit words carry H.
+template <int T, int ND>
+__device__ __forceinline__ int residue_byte(const ScaledDigits& g, const DigitCoefs& cf) {
   constexpr int m = ModConst<T>::m;
   if constexpr (m == 256) {
-    return l[0];
+    return g.lo;  // low byte of A' in two's complement
   } else {
-    int z = l[0];
-#pragma unroll
-    for (int k = 1; k <= NLHI; ++k) z = mad_i24(l[k], limb_coef(T, k), z);
+    // z = lo + sum_k d_k rho_m(2^(22 + 8 k)) = A' (mod m), |z| < 2^22 + 8 * 128 * 127 < 2^23
+    int z = __builtin_amdgcn_sdot4(static_cast<int>(g.w0), cf.c[T][0], g.lo, true);
+    if constexpr (ND > 1) z = __builtin_amdgcn_sdot4(static_cast<int>(g.w1), cf.c[T][1], z, true);
     // y = 1.5 * 2^23 + round(z / m): |z| < 2^23, so z / m is within 1/(2m) of z * inv
     // and never within 1/(2m) of a half-integer (m odd): the rounding is exact.
     const float y = __builtin_fmaf(static_cast<float>(z), ModConst<T>::inv, 12582912.0f);
@@ -113,16 +119,17 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
   return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
-template <int S, int NLHI, int T>
-__device__ __forceinline__ void store_residues(const int (&l)[16][NLHI + 1], int8_t* dst, long plane) {
+template <int S, int ND, int T>
+__device__ __forceinline__ void store_residues(const ScaledDigits (&g)[16], const DigitCoefs& cf, int8_t* dst,
+                                               long plane) {
   if constexpr (T < S) {
     int rr[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) rr[k] = residue_byte<T, NLHI>(l[k]);
+    for (int k = 0; k < 16; ++k) rr[k] = residue_byte<T, ND>(g[k], cf);
     uint4 v = make_uint4(pack4(rr[0], rr[1], rr[2], rr[3]), pack4(rr[4], rr[5], rr[6], rr[7]),
                          pack4(rr[8], rr[9], rr[10], rr[11]), pack4(rr[12], rr[13], rr[14], rr[15]));
     *reinterpret_cast<uint4*>(dst + T * plane) = v;
-    store_residues<S, NLHI, T + 1>(l, dst, plane);
+    store_residues<S, ND, T + 1>(g, cf, dst, plane);
   }
 }
 
@@ -130,7 +137,7 @@ __device__ __forceinline__ void store_residues(const int (&l)[16][NLHI + 1], int
 // thread mapping owner_rows_of_a (the thread's 16 elements of line i are
 // l = 256 blk + L + 16 k).  The validation dump of the scaled operand receives element
 // (line, l) at ap_dump[line dls + l dks].
-template <int S, int NLHI, bool DUMP>
+template <int S, int ND, bool DUMP>
 __global__ __launch_bounds__(256) void residues_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
                                                             const int* __restrict__ dsc, int8_t* __restrict__ at,
                                                             long plane, int q_pad, double* __restrict__ ap_dump,
@@ -139,24 +146,24 @@ __global__ __launch_bounds__(256) void residues_rows_kernel(const double* __rest
   const int i = own.row;
   const bool row_ok = i < p;
   const int scale = row_ok ? dsc[i] : 0;
-  int l[16][NLHI + 1];
+  ScaledDigits g[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int col = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = row_ok && col < q;
     const double x = ok ? A[i + static_cast<long>(col) * lda] : 0.0;
     double apv;
-    scaled_limbs<NLHI>(x, scale, l[k], DUMP ? &apv : nullptr);
+    g[k] = scaled_digits(x, scale, DUMP ? &apv : nullptr);
     if constexpr (DUMP) {
       if (ok) ap_dump[i * dls + col * dks] = apv;
     }
   }
-  store_residues<S, NLHI, 0>(l, at + operand_chunk_offset(i, own.blk, own.slot, q_pad), plane);
+  store_residues<S, ND, 0>(g, load_coefs<S, ND>(), at + operand_chunk_offset(i, own.blk, own.slot, q_pad), plane);
 }
 
 // Contiguous lines (columns of B, or rows of op(A) = A^T); thread mapping
 // owner_cols_of_b.  Dump as in residues_rows_kernel.
-template <int S, int NLHI, bool DUMP>
+template <int S, int ND, bool DUMP>
 __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                             const int* __restrict__ bsc, int8_t* __restrict__ bt,
                                                             long plane, int q_pad, double* __restrict__ bp_dump,
@@ -166,19 +173,19 @@ __global__ __launch_bounds__(256) void residues_cols_kernel(const double* __rest
   const bool col_ok = j < r;
   const int scale = col_ok ? bsc[j] : 0;
   const double* col = B + static_cast<long>(col_ok ? j : 0) * ldb;
-  int l[16][NLHI + 1];
+  ScaledDigits g[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int row = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = col_ok && row < q;
     const double x = ok ? col[row] : 0.0;
     double bpv;
-    scaled_limbs<NLHI>(x, scale, l[k], DUMP ? &bpv : nullptr);
+    g[k] = scaled_digits(x, scale, DUMP ? &bpv : nullptr);
     if constexpr (DUMP) {
       if (ok) bp_dump[j * dls + row * dks] = bpv;
     }
   }
-  store_residues<S, NLHI, 0>(l, bt + operand_chunk_offset(j, own.blk, own.slot, q_pad), plane);
+  store_residues<S, ND, 0>(g, load_coefs<S, ND>(), bt + operand_chunk_offset(j, own.blk, own.slot, q_pad), plane);
 }
 
 // Residue planes of one operand (nlines_pad rows); dump element (line, l) at
@@ -200,7 +207,7 @@ static void residues_lines(const Operand& o, int nlines, int nlines_pad, int q, 
 template <int S, bool ACCU>
 static void launch_residues_s(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump,
                               hipStream_t st) {
-  constexpr int NL = nl_hi(S, ACCU);
+  constexpr int NL = digit_words(S, ACCU);
   if (w.q_pad == 0) return;
   // A' dump: column-major p x q (ld p); B' dump: column-major q x r (ld q); each operand
   // runs the dumping kernel only when its own dump is requested

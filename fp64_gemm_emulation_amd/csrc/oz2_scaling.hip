@@ -31,29 +31,36 @@ __global__ void fill_u32_kernel(unsigned* __restrict__ p, unsigned v, long n) {
 }
 
 // Lines that are rows of a column-major matrix (rows of A, or columns of op(B) = B^T):
-// 64 lines (one per lane) x one kChunk block per workgroup; wave w reads l in
-// [c kChunk + 64 w, +64).  Each load instruction reads 64 consecutive rows of one
-// column.  MAXONLY: only the block max-abs exponents are produced.
+// kStatsRowGroups x 64 lines (one per lane) x one kChunk block per workgroup; the
+// kStatsColGroups waves of a row group split the block's columns, wave w reading
+// l in [c kChunk + kStatsCols w, +kStatsCols).  Each load instruction reads 64
+// consecutive rows of one column.  MAXONLY: only the block max-abs exponents are produced.
+constexpr int kStatsRowGroups = 1;
+constexpr int kStatsColGroups = 8;
+constexpr int kStatsCols = kChunk / kStatsColGroups;
+constexpr int kStatsThreads = kWave * kStatsRowGroups * kStatsColGroups;
 template <bool MAXONLY>
-__global__ __launch_bounds__(256) void stats_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
-                                                         int nch, int* __restrict__ part_e,
-                                                         double* __restrict__ part_s,
-                                                         unsigned* __restrict__ flags) {
-  __shared__ int sh_e[4][kWave];
-  __shared__ double sh_s[4][kWave];
+__global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double* __restrict__ A, long lda, int p,
+                                                                   int q, int nch, int* __restrict__ part_e,
+                                                                   double* __restrict__ part_s,
+                                                                   unsigned* __restrict__ flags) {
+  __shared__ int sh_e[kStatsRowGroups][kStatsColGroups][kWave];
+  __shared__ double sh_s[kStatsRowGroups][kStatsColGroups][kWave];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int i = blockIdx.x * kWave + lane;
+  const int wave = threadIdx.x >> 6;
+  const int g = wave / kStatsColGroups;
+  const int w = wave % kStatsColGroups;
+  const int i = (blockIdx.x * kStatsRowGroups + g) * kWave + lane;
   const int c = blockIdx.y;
-  const int l0 = c * kChunk + w * kWave;
+  const int l0 = c * kChunk + w * kStatsCols;
   const bool row_ok = i < p;
   const double* base = A + (row_ok ? i : 0) + static_cast<long>(l0) * lda;
 
-  double v[kWave];
+  double v[kStatsCols];
   int emax = kNoExp;
   bool bad = false;
 #pragma unroll
-  for (int k = 0; k < kWave; ++k) {
+  for (int k = 0; k < kStatsCols; ++k) {
     double x = 0.0;
     if (row_ok && l0 + k < q) x = base[static_cast<long>(k) * lda];
     const bool nf = is_nonfinite(x);
@@ -63,26 +70,32 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const double* __restric
     emax = max(emax, exponent_of(x));
   }
   if (bad) atomicOr(flags, kFlagNonFinite);
-  sh_e[w][lane] = emax;
+  sh_e[g][w][lane] = emax;
   __syncthreads();
-  const int ec = max(max(sh_e[0][lane], sh_e[1][lane]), max(sh_e[2][lane], sh_e[3][lane]));
+  int ec = kNoExp;
+#pragma unroll
+  for (int u = 0; u < kStatsColGroups; ++u) ec = max(ec, sh_e[g][u][lane]);
   if constexpr (MAXONLY) {
     if (w == 0 && row_ok) part_e[static_cast<long>(i) * nch + c] = ec;
     return;
   } else {
-    double acc = 0.0;  // exact: at most 64 * 2^40
+    double acc = 0.0;  // exact: at most kStatsCols * 2^40
     if (ec != kNoExp) {
 #pragma unroll
-      for (int k = 0; k < kWave; ++k) {
+      for (int k = 0; k < kStatsCols; ++k) {
         const double u = ceil_scaled_abs(v[k], exponent_of(v[k]), kFBits - ec);
         acc = fma(u, u, acc);
       }
     }
-    sh_s[w][lane] = acc;
+    sh_s[g][w][lane] = acc;
     __syncthreads();
     if (w == 0 && row_ok) {
+      // exact integer sums below 2^49: the grouping does not matter
+      double tot = 0.0;
+#pragma unroll
+      for (int u = 0; u < kStatsColGroups; ++u) tot += sh_s[g][u][lane];
       part_e[static_cast<long>(i) * nch + c] = ec;
-      part_s[static_cast<long>(i) * nch + c] = (sh_s[0][lane] + sh_s[1][lane]) + (sh_s[2][lane] + sh_s[3][lane]);
+      part_s[static_cast<long>(i) * nch + c] = tot;
     }
   }
 }
@@ -302,8 +315,9 @@ static void stats_lines(const Operand& o, int nlines, int q, int nch, int* pe, d
     dim3 grid(nlines, blocks_for(nch, 4 * kColBlocks));
     hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps, flags);
   } else {
-    dim3 grid(blocks_for(nlines, kWave), nch);
-    hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, nlines, q, nch, pe, ps, flags);
+    dim3 grid(blocks_for(nlines, kWave * kStatsRowGroups), nch);
+    hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(kStatsThreads), 0, st, o.ptr, o.ld, nlines, q, nch, pe,
+                       ps, flags);
   }
 }
 
