@@ -3,11 +3,11 @@
 //
 // X is computed exactly: with W_t = (M/m_t) ((M/m_t)^-1 mod m_t),
 //   X = sum_t R_t W_t - k M,   k = round(sum_t R_t W_t / M).
-// W_t and M are split into 32-bit limbs held in doubles, so every limb sum is an exact
-// FP64 integer FMA chain (each partial sum < 20 * 2^8 * 2^32 < 2^53).  k comes from the two
+// W_t and M are split into limbs of at most 40 bits held in doubles, so every limb sum is
+// an exact FP64 integer FMA chain (each partial sum < 20 * 2^8 * 2^40 < 2^53).  k comes from the two
 // top limb sums (the lower limbs cannot move the quotient across a half-integer: the
-// scalings keep |X| <= 2^tau).  The limbs are carried into [0, 2^32) with floor, which
-// makes them the two's-complement words of X, then rounded to FP64 with one
+// scalings keep |X| <= 2^tau).  The lower limbs are carried into [0, 2^kW) with floor and
+// the result rounded to FP64 with one
 // round-to-nearest-even and scaled by 2^-(d_i + b_j) with ldexp (exact unless the result is
 // subnormal); oz2_crt_round.hpp holds that step and why one FMA rounding is enough.  The
 // stored value is alpha Chat when beta = 0 (C is not read) and fma(alpha, Chat, RN(beta C))
@@ -72,17 +72,15 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ re
   for (int v = 0; v < kRowsPerThread; ++v) {
     const int i = min(i0 + v, p - 1);  // rows past p (last group only) are computed, not stored
     crt_reduce<S>(acc[v]);
-    crt_normalize<L>(acc[v]);
+    crt_normalize<L, CrtTable<S>::kW>(acc[v]);
     if (DUMPX && i0 + v < p) {
-      // the normalised limbs are the two's-complement words of X (top word signed)
-      const int top = static_cast<int>(acc[v][L - 1]);
+      uint32_t wd[5];
+      crt_words<L, CrtTable<S>::kW>(acc[v], wd);
       uint32_t* xd = x_dump + (static_cast<long>(j) * p + i) * 5;
 #pragma unroll
-      for (int k = 0; k < 5; ++k)
-        xd[k] = k < L - 1 ? static_cast<uint32_t>(acc[v][k])
-                          : (k == L - 1 ? static_cast<uint32_t>(top) : (top < 0 ? 0xFFFFFFFFu : 0u));
+      for (int k = 0; k < 5; ++k) xd[k] = wd[k];
     }
-    out[v] = crt_round<L, CrtTable<S>::kTopExp>(acc[v], -(d[i] + bj));
+    out[v] = crt_round<L, CrtTable<S>::kW, CrtTable<S>::kTopExp>(acc[v], -(d[i] + bj));
   }
   double* dst = C + i0 + static_cast<long>(j) * ldc;
   if (beta != 0.0) {

@@ -1,24 +1,26 @@
 // oz2_crt_round.hpp -- the per-output arithmetic of the reconstruction ("Profiling Ozaki
 // II: The Cost Behind Fast INT8 GEMMs", Part I section 1, red stage), callable from device
 // and host code:
-//   crt_accumulate  acc[k] += R_t W_t[k]  (32-bit limbs of the CRT weights, exact FMAs)
+//   crt_accumulate  acc[k] += R_t W_t[k]  (kW-bit limbs of the CRT weights, exact FMAs)
 //   crt_reduce      acc -= k M with k the nearest integer to sum_t R_t W_t / M
-//   crt_normalize   acc[0..L-2] -> [0, 2^32), carries moved up (the two's-complement words)
+//   crt_normalize   acc[0..L-2] -> [0, 2^kW), carries moved up
 //   crt_round       RN(X) 2^scale
-// The limb sums X = sum_k acc[k] 2^(32 k) stay exact integers below 2^53 in magnitude.
+//   crt_words       the 32-bit two's-complement words of X (validation)
+// The limb sums X = sum_k acc[k] 2^(kW k) stay exact integers below 2^53 in magnitude.
 //
 // Rounding without an integer detour.  After normalisation,
-//   H_j = floor(X / 2^(32 j)) = H_{j+1} 2^32 + acc[j],   H_{L-1} = acc[L-1].
-// If |H_j| < 2^21, H_{j-1} is below 2^53 and exact.  Take the largest level j >= 2 with
-// |H_j| >= 2^21: then |X| >= 2^(32 j + 20), so the final unit in the last place is at least
-// 2^(32 j - 32) and every rounding boundary (the doubles and the midpoints between them) is
-// a multiple of 2^(32 j - 33) = 2^(32 (j - 2) + 31).  Replacing the limbs below level j - 1
-// by bit 31 of acc[j-2] plus a sticky 2^30 when anything below that bit is nonzero gives a
-// value Xh in the same cell of that grid as X (equal to X exactly when X lies on it), so
-// RN(Xh) = RN(X); Xh = (H_j 2^64 + acc[j-1] 2^32 + hat) 2^(32 (j-2)) needs one rounding, in
-// one FMA, because acc[j-1] 2^32 + hat has at most 34 significant bits.  If no level
-// triggers, |H_1| < 2^53 and RN(X) = RN(H_1 2^32 + acc[0]) is again one FMA.  Levels whose
-// H cannot reach 2^21 (kTopExp bounds |H_{L-1}| by 2^kTopExp) are skipped at compile time.
+//   H_j = floor(X / 2^(kW j)) = H_{j+1} 2^kW + acc[j],   H_{L-1} = acc[L-1].
+// If |H_j| < 2^(52 - kW), H_{j-1} is below 2^53 and exact.  Take the largest level j >= 2
+// with |H_j| >= 2^(52 - kW): then |X| >= 2^(kW (j - 1) + 51), so the final unit in the last
+// place is at least 2^(kW (j - 1) - 1) and every rounding boundary (the doubles and the
+// midpoints between them) is a multiple of 2^(kW (j - 2) + kW - 2).  Replacing the limbs below
+// level j - 1 by the top two bits of acc[j-2] plus a sticky 2^(kW - 3) when anything below
+// them is nonzero gives a value Xh in the same cell of that grid as X (equal to X exactly
+// when X lies on it), so RN(Xh) = RN(X); Xh = (H_j 2^(2 kW) + acc[j-1] 2^kW + hat)
+// 2^(kW (j-2)) needs one rounding, in one FMA, because acc[j-1] 2^kW + hat has at most
+// kW + 3 significant bits.  If no level triggers, |H_1| < 2^53 and
+// RN(X) = RN(H_1 2^kW + acc[0]) is again one FMA.  Levels whose H cannot reach the
+// threshold (kTopExp bounds |H_{L-1}| by 2^kTopExp) are skipped at compile time.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cmath>
@@ -54,44 +56,75 @@ __host__ __device__ constexpr double pow2i(int e) {
   return x;
 }
 
-// acc[0..L-2] -> [0, 2^32) with the carries moved up; X is unchanged and acc[L-1] becomes
-// floor(X / 2^(32 (L-1))).  Exact: power-of-two scalings, floor and integer sums < 2^53.
-template <int L>
+// acc[0..L-2] -> [0, 2^W) with the carries moved up; X is unchanged and acc[L-1] becomes
+// floor(X / 2^(W (L-1))).  Exact: power-of-two scalings, floor and integer sums < 2^53.
+template <int L, int W>
 __host__ __device__ inline void crt_normalize(double (&acc)[L]) {
+  constexpr double kUp = pow2i(W), kDown = 1.0 / pow2i(W);
 #pragma unroll
   for (int k = 0; k + 1 < L; ++k) {
-    const double cy = floor(acc[k] * 0x1p-32);
-    acc[k] = fma(-cy, 0x1p32, acc[k]);
+    const double cy = floor(acc[k] * kDown);
+    acc[k] = fma(-cy, kUp, acc[k]);
     acc[k + 1] += cy;
   }
 }
 
 // RN(X) * 2^scale for normalised limbs (exact scaling unless the result is subnormal).
-template <int L, int kTopExp>
+template <int L, int W, int kTopExp>
 __host__ __device__ inline double crt_round(const double (&a)[L], int scale) {
   if constexpr (L == 1) {
     return ldexp(a[0], scale);  // |X| < 2^53: exact
   } else {
+    constexpr double kUp = pow2i(W), kUp2 = pow2i(2 * W);
+    constexpr double kThr = pow2i(52 - W);
+    constexpr double kTop2 = 1.0 / pow2i(W - 2), kBit = pow2i(W - 2), kSticky = pow2i(W - 3);
     double h[L];
     h[L - 1] = a[L - 1];
 #pragma unroll
-    for (int j = L - 1; j >= 2; --j) h[j - 1] = fma(h[j], 0x1p32, a[j - 1]);
-    double z = fma(h[1], 0x1p32, a[0]);
+    for (int j = L - 1; j >= 2; --j) h[j - 1] = fma(h[j], kUp, a[j - 1]);
+    double z = fma(h[1], kUp, a[0]);
 #pragma unroll
     for (int j = 2; j < L; ++j) {
-      if (j == L - 1 && kTopExp < 21) continue;
-      const double b = floor(a[j - 2] * 0x1p-31);
-      bool sticky = fma(-b, 0x1p31, a[j - 2]) != 0.0;
+      if (j == L - 1 && kTopExp < 52 - W) continue;
+      const double b = floor(a[j - 2] * kTop2);  // top two bits of the limb below
+      bool sticky = fma(-b, kBit, a[j - 2]) != 0.0;
 #pragma unroll
       for (int k = 0; k < j - 2; ++k) sticky = sticky || a[k] != 0.0;
-      const double hat = fma(b, 0x1p31, sticky ? 0x1p30 : 0.0);
-      const double u = fma(a[j - 1], 0x1p32, hat);
-      double zj = fma(h[j], 0x1p64, u);
-      if (j > 2) zj *= pow2i(32 * (j - 2));  // exact
-      if (fabs(h[j]) >= 0x1p21) z = zj;
+      const double hat = fma(b, kBit, sticky ? kSticky : 0.0);
+      const double u = fma(a[j - 1], kUp, hat);
+      double zj = fma(h[j], kUp2, u);
+      if (j > 2) zj *= pow2i(W * (j - 2));  // exact
+      if (fabs(h[j]) >= kThr) z = zj;
     }
     return ldexp(z, scale);
   }
+}
+
+// The five 32-bit two's-complement words (little-endian) of X = sum_k a[k] 2^(W k) for
+// normalised limbs (a[0..L-2] in [0, 2^W), |a[L-1]| < 2^40): the limbs are shifted into a
+// 192-bit integer from the top down.
+template <int L, int W>
+__host__ __device__ inline void crt_words(const double (&a)[L], uint32_t (&out)[5]) {
+  const double th = floor(a[L - 1] * 0x1p-32);
+  const uint64_t top = (static_cast<uint64_t>(static_cast<int64_t>(th)) << 32) |
+                       static_cast<uint32_t>(fma(-th, 0x1p32, a[L - 1]));
+  uint64_t x[3] = {top, (top >> 63) != 0 ? ~0ull : 0ull, (top >> 63) != 0 ? ~0ull : 0ull};
+#pragma unroll
+  for (int k = L - 2; k >= 0; --k) {
+    x[2] = (x[2] << W) | (x[1] >> (64 - W));
+    x[1] = (x[1] << W) | (x[0] >> (64 - W));
+    x[0] = x[0] << W;
+    const double hi = floor(a[k] * 0x1p-32);
+    const uint64_t v = (static_cast<uint64_t>(hi) << 32) | static_cast<uint32_t>(fma(-hi, 0x1p32, a[k]));
+    const uint64_t s0 = x[0] + v;
+    const uint64_t c0 = s0 < v ? 1ull : 0ull;
+    x[0] = s0;
+    const uint64_t s1 = x[1] + c0;
+    x[2] += s1 < c0 ? 1ull : 0ull;
+    x[1] = s1;
+  }
+#pragma unroll
+  for (int k = 0; k < 5; ++k) out[k] = static_cast<uint32_t>(x[k / 2] >> (32 * (k % 2)));
 }
 
 }  // namespace oz2

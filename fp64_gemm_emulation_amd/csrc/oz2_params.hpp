@@ -188,21 +188,36 @@ constexpr int digit_coefs(int t, int w) {
 
 // ---------------------------------------------------------------------------
 // CRT constants: X = sum_t R_t W_t - k M, W_t = (M / m_t) * ((M / m_t)^-1 mod m_t).
-// W_t and M are held as 32-bit limbs stored in doubles so the weighted sums are exact
-// FP64 integer FMAs (every partial sum stays below 20 * 2^8 * 2^32 < 2^53).  k is the
-// nearest integer to sum_t R_t W_t / M, estimated from the two top limb sums alone:
-// k = rint(acc[L-1] q1 + acc[L-2] q0) with q1 = 2^(32 (L-1)) / M, q0 = 2^(32 (L-2)) / M.
-// The limbs left out add less than 20 * 255 * 2^(32 (L-2)) * (1 + 2^-31) / M < 2^-19
-// (M > 2^(32 (L-1))), and the scalings keep |X| <= 2^tau, which puts the exact quotient at
-// least 0.014 from a half-integer for every s: the estimate rounds to k.
+// W_t and M are split into L limbs of kW <= 40 bits (the fewest limbs of at most 40 bits
+// that hold M), stored in doubles, so the weighted sums are exact FP64 integer FMAs:
+// every partial sum stays below 20 * 2^8 * 2^40 < 2^53.  k is the nearest integer to
+// sum_t R_t W_t / M, estimated from the two top limb sums alone,
+// k = rint(acc[L-1] q1 + acc[L-2] q0) with q1 = 2^(kW (L-1)) / M, q0 = 2^(kW (L-2)) / M.
+// The limbs left out add less than 20 * 255 * 2^(kW (L-2)) * (1 + 2^-kW) / M
+// <= 5100 * 2^-kW (M > 2^(kW (L-1))) to the quotient, below 4e-5 wherever L >= 3, and the
+// scalings keep |X| <= 2^tau, which puts the exact quotient at least 0.014 from a
+// half-integer for every s: the estimate rounds to k.
 // ---------------------------------------------------------------------------
-constexpr int crt_limbs(int S) { return (big_bitlen(modulus_product(S)) + 31) / 32; }
+constexpr int crt_bits(int S) { return big_bitlen(modulus_product(S)); }
+constexpr int crt_limbs(int S) { return (crt_bits(S) + 39) / 40; }
+constexpr int crt_width(int S) { return (crt_bits(S) + crt_limbs(S) - 1) / crt_limbs(S); }
+
+// bits [lo, lo + n) of a, n <= 40
+constexpr uint64_t big_bits(Big a, int lo, int n) {
+  uint64_t v = 0;
+  for (int b = 0; b < n; ++b) {
+    const int pos = lo + b;
+    if (pos < 32 * kBigLimbs && ((a.w[pos / 32] >> (pos % 32)) & 1u)) v |= 1ull << b;
+  }
+  return v;
+}
 
 template <int S>
 struct CrtTable {
   static constexpr int L = crt_limbs(S);
-  // |floor(X / 2^(32 (L-1)))| <= 2^kTopExp for |X| <= 2^tau
-  static constexpr int kTopExp = tau_of(S) - 32 * (L - 1);
+  static constexpr int kW = crt_width(S);
+  // |floor(X / 2^(kW (L-1)))| <= 2^kTopExp for |X| <= 2^tau
+  static constexpr int kTopExp = tau_of(S) - kW * (L - 1);
   double w[S][L];
   double m[L];
   double q1, q0;
@@ -212,25 +227,39 @@ template <int S>
 constexpr CrtTable<S> make_crt() {
   CrtTable<S> tab{};
   constexpr int L = CrtTable<S>::L;
+  constexpr int W = CrtTable<S>::kW;
   Big M = modulus_product(S);
   double md = 0.0;
   for (int k = kBigLimbs - 1; k >= 0; --k) md = md * 0x1p32 + static_cast<double>(M.w[k]);
-  for (int k = 0; k < L; ++k) tab.m[k] = static_cast<double>(M.w[k]);
+  for (int k = 0; k < L; ++k) tab.m[k] = static_cast<double>(big_bits(M, W * k, W));
   for (int t = 0; t < S; ++t) {
     uint32_t mt = static_cast<uint32_t>(modulus(t));
     Big rest = product_except(S, t);
     uint32_t inv = inv_mod(big_mod_small(rest, mt), mt);
     Big w = big_mul_small(rest, inv);
-    for (int k = 0; k < L; ++k) tab.w[t][k] = static_cast<double>(w.w[k]);
+    for (int k = 0; k < L; ++k) tab.w[t][k] = static_cast<double>(big_bits(w, W * k, W));
   }
   double p1 = 1.0;
-  for (int k = 0; k < 32 * (L - 1); ++k) p1 *= 2.0;
+  for (int k = 0; k < W * (L - 1); ++k) p1 *= 2.0;
   tab.q1 = p1 / md;
-  tab.q0 = L >= 2 ? tab.q1 * 0x1p-32 : 0.0;
+  double p0 = 1.0;
+  for (int k = 0; k < W * (L - 2); ++k) p0 *= 2.0;
+  tab.q0 = L >= 2 ? p0 / md : 0.0;
   return tab;
 }
 
-static_assert(CrtTable<kMaxS>::kTopExp <= 30 && CrtTable<kMinS>::L == 1, "top limb fits int32");
+constexpr bool crt_layout_ok() {
+  for (int s = kMinS; s <= kMaxS; ++s) {
+    const int L = crt_limbs(s), W = crt_width(s);
+    if (W > 40 || W * L < crt_bits(s)) return false;      // limbs hold M, sums exact
+    if (L >= 2 && crt_bits(s) - 1 < W * (L - 1)) return false;  // M > 2^(W (L-1))
+    if (L >= 3 && W < 27) return false;                  // neglected limbs < 4e-5
+    if (tau_of(s) - W * (L - 1) > 40) return false;      // top limb below 2^40
+    if (L == 1 && crt_bits(s) > 53) return false;
+  }
+  return true;
+}
+static_assert(crt_layout_ok(), "CRT limb layout");
 
 template <int S>
 inline constexpr CrtTable<S> kCrt = make_crt<S>();

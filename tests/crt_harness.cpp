@@ -15,12 +15,11 @@ static void one(int scale, const unsigned* res) {
   for (int k = 0; k < L; ++k) acc[k] = 0.0;
   for (int t = 0; t < S; ++t) oz2::crt_accumulate<S>(acc, static_cast<double>(res[t]), t);
   oz2::crt_reduce<S>(acc);
-  oz2::crt_normalize<L>(acc);
-  const int top = static_cast<int>(acc[L - 1]);
-  unsigned w[5];
-  for (int k = 0; k < 5; ++k)
-    w[k] = k < L - 1 ? static_cast<unsigned>(acc[k]) : (k == L - 1 ? static_cast<unsigned>(top) : (top < 0 ? ~0u : 0u));
-  const double z = oz2::crt_round<L, oz2::CrtTable<S>::kTopExp>(acc, scale);
+  constexpr int W = oz2::CrtTable<S>::kW;
+  oz2::crt_normalize<L, W>(acc);
+  uint32_t w[5];
+  oz2::crt_words<L, W>(acc, w);
+  const double z = oz2::crt_round<L, W, oz2::CrtTable<S>::kTopExp>(acc, scale);
   unsigned long long bits;
   std::memcpy(&bits, &z, sizeof bits);
   std::printf("%08x %08x %08x %08x %08x %016llx\n", w[0], w[1], w[2], w[3], w[4], bits);

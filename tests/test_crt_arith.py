@@ -87,15 +87,14 @@ def cases_for(s, rng):
         x = 2**e + 2 ** (e - 53)                              # tie just above a power of two
         if x <= 2**T:
             xs.update({x, -x, x + 1, x - 1})
-    # every (last bit, round bit, sticky) combination at random magnitudes, and in bands
-    # around the level switches (|X| within 2^(32 j) of 2^(32 j + 20) and 2^(32 j + 21))
+    # every (last bit, round bit, sticky) combination at random magnitudes, and in a band
+    # around every power of two (where a limb-level switch of the rounding can sit, for any
+    # limb width): |X| within 2^(e - 12) of 2^e
     mags = [rng.randint(2**55, 2**T) for _ in range(60)] if T > 56 else []
-    for j in range(2, 6):
-        for c in (2 ** (32 * j + 20), 2 ** (32 * j + 21)):
-            for _ in range(12):
-                v = c + rng.randint(-(2 ** (32 * j)), 2 ** (32 * j))
-                if 2**55 < v <= 2**T:
-                    mags.append(v)
+    for e in range(56, T + 1):
+        for v in (2**e - rng.randint(1, 2 ** (e - 12)), 2**e + rng.randint(0, 2 ** (e - 12))):
+            if 2**55 < v <= 2**T:
+                mags.append(v)
     for v in mags:
         for lsb in (0, 1):
             for rnd in (0, 1):
@@ -136,13 +135,22 @@ def test_crt_arith_exact_words_and_rounding(harness, s):
     assert not bad, f"s={s}: {len(bad)} of {len(xs)} differ, first: X={bad[0][0]} got {bad[0][1]} want {bad[0][2]}"
 
 
-def test_crt_arith_cases_cover_ties_and_levels():
-    """The case list holds exact ties and crosses every rounding level the largest s reaches."""
+def test_crt_arith_cases_cover_ties_and_binades():
+    """The case list holds exact ties, and every rounding-bit pattern with both signs in
+    every binade from 2^56 to 2^tau, for the largest s."""
     rng = random.Random(7)
     xs = cases_for(20, rng)
     ties = [x for x in xs if abs(x).bit_length() > 54 and
             (abs(x) >> (abs(x).bit_length() - 54)) & 1 and
             abs(x) % (1 << (abs(x).bit_length() - 54)) == 0]
     assert len(ties) > 100
-    levels = {j for j in range(2, 5) for x in xs if abs(x >> (32 * j)) >= 2**21}
-    assert levels == {2, 3, 4}
+    T = tau(math.prod(moduli(20)))
+    seen = set()
+    for x in xs:
+        e = abs(x).bit_length()
+        if e > 56:
+            low = e - 54
+            seen.add((e, x < 0, (abs(x) >> (low + 1)) & 1, (abs(x) >> low) & 1, abs(x) % (1 << low) != 0))
+    missing = [(e, neg, a, b, c) for e in range(58, T) for neg in (False, True)
+               for a in (0, 1) for b in (0, 1) for c in (False, True) if (e, neg, a, b, c) not in seen]
+    assert not missing, missing[:5]
