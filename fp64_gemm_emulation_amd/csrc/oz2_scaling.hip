@@ -14,7 +14,11 @@
 // accu (same page, section 2 and 5.1 "accu"): |A| and |B| quantized upward into
 // integers in [0, 2^kQBits] relative to each line's max-abs exponent, one INT8 bound
 // GEMM (oz2_gemm.hip), row / column maxima rho, gamma of its output, then
-// d = floor((tau - ceil(log2 max(rho, 1))) / 2) + kQBits - e.
+// d = floor((tau - ceil(log2 max(rho, 1))) / 2) + kQBits - e.  The quantized inputs are
+// formed without a second pass over A and B: the max-abs pass quantizes each element
+// against its block's exponent e_c while the values are in registers, and a byte pass
+// divides by 2^(e - e_c) with rounding up once the line exponent e is known
+// (ceil(ceil(y) / 2^k) = ceil(y / 2^k)).
 #include "oz2_common.hpp"
 #include "oz2_internal.hpp"
 
@@ -43,7 +47,8 @@ template <bool MAXONLY>
 __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double* __restrict__ A, long lda, int p,
                                                                    int q, int nch, int* __restrict__ part_e,
                                                                    double* __restrict__ part_s,
-                                                                   unsigned* __restrict__ flags) {
+                                                                   unsigned* __restrict__ flags,
+                                                                   int8_t* __restrict__ qout, int q_pad) {
   __shared__ int sh_e[kStatsRowGroups][kStatsColGroups][kWave];
   __shared__ double sh_s[kStatsRowGroups][kStatsColGroups][kWave];
   const int lane = threadIdx.x & 63;
@@ -77,6 +82,33 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
   for (int u = 0; u < kStatsColGroups; ++u) ec = max(ec, sh_e[g][u][lane]);
   if constexpr (MAXONLY) {
     if (w == 0 && row_ok) part_e[static_cast<long>(i) * nch + c] = ec;
+    if (qout != nullptr) {
+      // block-quantized bound input ceil(|a| 2^(kQBits - e_c)) in the operand tile layout:
+      // element 32 w + k of the block goes to chunk slot k mod 16, byte 2 w + k / 16
+      static_assert(kStatsColGroups == 8 && kStatsRowGroups == 1, "one row group, two bytes per wave and slot");
+      __shared__ uint16_t sq[kWave][16][8];
+#pragma unroll
+      for (int L = 0; L < 16; ++L) {
+        uint32_t q0 = 0, q1 = 0;
+        if (ec != kNoExp) {
+          q0 = static_cast<uint32_t>(ceil_scaled_abs(v[L], exponent_of(v[L]), kQBits - ec));
+          q1 = static_cast<uint32_t>(ceil_scaled_abs(v[L + 16], exponent_of(v[L + 16]), kQBits - ec));
+        }
+        sq[lane][L][w] = static_cast<uint16_t>(q0 | (q1 << 8));
+      }
+      __syncthreads();
+      // 64 rows x 16 chunks; consecutive threads fill one 64-byte row segment, then the next
+      // row, so each wave stores 1 KiB of one stage tile contiguously
+      const int row0 = blockIdx.x * kWave;
+#pragma unroll
+      for (int ci = threadIdx.x; ci < kWave * 16; ci += kStatsThreads) {
+        const int rrow = (ci >> 2) & (kWave - 1);
+        const int rr = row0 + rrow;
+        const int slot = 4 * (ci >> 8) + ((ci & 3) ^ operand_swizzle(rr & 15));
+        *reinterpret_cast<uint4*>(qout + operand_chunk_offset(rr, c, slot, q_pad)) =
+            *reinterpret_cast<const uint4*>(&sq[rrow][slot][0]);
+      }
+    }
     return;
   } else {
     double acc = 0.0;  // exact: at most kStatsCols * 2^40
@@ -110,13 +142,15 @@ template <bool MAXONLY>
 __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                          int nch, int* __restrict__ part_e,
                                                          double* __restrict__ part_s,
-                                                         unsigned* __restrict__ flags) {
+                                                         unsigned* __restrict__ flags,
+                                                         int8_t* __restrict__ qout, int q_pad) {
   // grid: x = column j, y = groups of 4 kColBlocks blocks; one wave per (j, kColBlocks blocks)
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x;
   const int c0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kColBlocks;
   if (c0 >= nch) return;  // whole wave
-  const double* col = B + static_cast<long>(j) * ldb;
+  const bool col_ok = j < r;  // columns up to the padded count when the bound input is written
+  const double* col = B + static_cast<long>(col_ok ? j : 0) * ldb;
   double v[kColBlocks][4];
   bool bad = false;
 #pragma unroll
@@ -124,7 +158,7 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int l = (c0 + b) * kChunk + lane + kWave * k;
-      double x = (c0 + b < nch && l < q) ? col[l] : 0.0;
+      double x = (col_ok && c0 + b < nch && l < q) ? col[l] : 0.0;
       const bool nf = is_nonfinite(x);
       bad |= nf;
       v[b][k] = nf ? 0.0 : x;
@@ -140,7 +174,33 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
     const int ec = wave_max(emax);
     const long slot = static_cast<long>(j) * nch + c;
     if constexpr (MAXONLY) {
-      if (lane == 0) part_e[slot] = ec;
+      if (lane == 0 && col_ok) part_e[slot] = ec;
+      if (qout != nullptr) {
+        // block-quantized bound input: element lane + 64 k goes to chunk slot lane mod 16,
+        // byte lane / 16 + 4 k; lane L < 16 gathers the words of lanes L + 16 g and
+        // transposes the 4 x 4 bytes into its chunk
+        uint32_t pk = 0;
+        if (ec != kNoExp) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            pk |= static_cast<uint32_t>(ceil_scaled_abs(v[b][k], exponent_of(v[b][k]), kQBits - ec)) << (8 * k);
+        }
+        const int L = lane & 15;
+        const uint32_t g0 = static_cast<uint32_t>(__shfl(static_cast<int>(pk), L, kWave));
+        const uint32_t g1 = static_cast<uint32_t>(__shfl(static_cast<int>(pk), L + 16, kWave));
+        const uint32_t g2 = static_cast<uint32_t>(__shfl(static_cast<int>(pk), L + 32, kWave));
+        const uint32_t g3 = static_cast<uint32_t>(__shfl(static_cast<int>(pk), L + 48, kWave));
+        // word k of the chunk = byte k of g0, g1, g2, g3
+        const uint32_t lo01 = __builtin_amdgcn_perm(g1, g0, 0x05010400u);  // g0.b0 g1.b0 g0.b1 g1.b1
+        const uint32_t hi01 = __builtin_amdgcn_perm(g1, g0, 0x07030602u);  // g0.b2 g1.b2 g0.b3 g1.b3
+        const uint32_t lo23 = __builtin_amdgcn_perm(g3, g2, 0x05010400u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(g3, g2, 0x07030602u);
+        const uint4 chunk = make_uint4(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                                       __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                                       __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                                       __builtin_amdgcn_perm(hi23, hi01, 0x07060302u));
+        if (lane < 16) *reinterpret_cast<uint4*>(qout + operand_chunk_offset(j, c, L, q_pad)) = chunk;
+      }
     } else {
       double acc = 0.0;
       if (ec != kNoExp) {
@@ -221,53 +281,33 @@ __global__ void max_exponents_kernel(int na, int nb, int nch, const int* __restr
 }
 
 // accu bound inputs of lines that are rows of a column-major matrix:
-// Abar_il = ceil(|a_il| 2^(kQBits - e_i)) in [0, 64], written in the tile-contiguous
-// operand layout (zeros in the padding); thread mapping owner_rows_of_a, the thread
-// covers l = 256 blk + L + 16 k.
-__global__ __launch_bounds__(256) void quant_rows_kernel(const double* __restrict__ A, long lda, int p, int q,
-                                                         int q_pad, const int* __restrict__ e_row,
-                                                         int8_t* __restrict__ abar) {
-  const ChunkOwner own = owner_rows_of_a();
-  const int i = own.row, blk = own.blk, L = own.slot;
-  const bool row_ok = i < p;
-  const int e = row_ok ? e_row[i] : kNoExp;
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
-  if (e != kNoExp) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int l = blk * kKPad + L + 16 * k;
-      double x = l < q ? A[i + static_cast<long>(l) * lda] : 0.0;
-      x = is_nonfinite(x) ? 0.0 : x;
-      const uint32_t qv = static_cast<uint32_t>(ceil_scaled_abs(x, exponent_of(x), kQBits - e));
-      packed[k >> 2] |= qv << (8 * (k & 3));
-    }
-  }
-  uint4* dst = reinterpret_cast<uint4*>(abar + operand_chunk_offset(i, blk, L, q_pad));
-  *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-}
-
-// accu bound inputs of contiguous lines; thread mapping owner_cols_of_b.
-__global__ __launch_bounds__(256) void quant_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
-                                                         int q_pad, const int* __restrict__ f_col,
-                                                         int8_t* __restrict__ bbar) {
-  const ChunkOwner own = owner_cols_of_b();
-  const int j = own.row, blk = own.blk, L = own.slot;
-  const bool col_ok = j < r;
-  const int f = col_ok ? f_col[j] : kNoExp;
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
-  if (f != kNoExp) {
-    const double* col = B + static_cast<long>(j) * ldb;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int l = blk * kKPad + L + 16 * k;
-      double x = l < q ? col[l] : 0.0;
-      x = is_nonfinite(x) ? 0.0 : x;
-      const uint32_t qv = static_cast<uint32_t>(ceil_scaled_abs(x, exponent_of(x), kQBits - f));
-      packed[k >> 2] |= qv << (8 * (k & 3));
-    }
-  }
-  uint4* dst = reinterpret_cast<uint4*>(bbar + operand_chunk_offset(j, blk, L, q_pad));
-  *dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+// accu bound input from its block-quantized form: the statistics pass wrote
+// Abar'_il = ceil(|a_il| 2^(kQBits - e_c)) with the block exponent e_c <= e_i, and
+// ceil(|a| 2^(kQBits - e_i)) = ceil(Abar' / 2^(e_i - e_c)) (nested ceilings by a power of
+// two).  Bytes are at most 64, so v + 2^kk - 1 stays below 256 and the four bytes of a word
+// are shifted together; kk = min(e_i - e_c, 7) (a shift by 7 or more leaves v > 0 ? 1 : 0).
+// grid: x = (lines x 4 chunks) / 256, y = the 4 stages of each 256-block.
+__global__ __launch_bounds__(256) void requant_kernel(int8_t* __restrict__ plane, int nlines, int nch, int q_pad,
+                                                      const int* __restrict__ e_line,
+                                                      const int* __restrict__ part_e) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int line = t >> 2;
+  if (line >= nlines) return;
+  const int blk = blockIdx.y >> 2;
+  const int e = e_line[line];
+  const int ec = part_e[static_cast<long>(line) * nch + blk];
+  if (e == kNoExp || ec == kNoExp || e == ec) return;  // zero chunk, or no shift
+  const int kk = min(e - ec, 7);
+  const int slot = 4 * (blockIdx.y & 3) + ((t & 3) ^ operand_swizzle(line & 15));
+  uint4* ptr = reinterpret_cast<uint4*>(plane + operand_chunk_offset(line, blk, slot, q_pad));
+  const uint32_t add = ((1u << kk) - 1u) * 0x01010101u;
+  const uint32_t mask = (0xFFu >> kk) * 0x01010101u;
+  uint4 x = *ptr;
+  x.x = ((x.x + add) >> kk) & mask;
+  x.y = ((x.y + add) >> kk) & mask;
+  x.z = ((x.z + add) >> kk) & mask;
+  x.w = ((x.w + add) >> kk) & mask;
+  *ptr = x;
 }
 
 // accu exponents from the bound-product maxima.
@@ -308,24 +348,37 @@ hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st
 
 // Block statistics of the lines of one operand (rows of op(A) or columns of op(B)).
 template <bool MAXONLY>
-static void stats_lines(const Operand& o, int nlines, int q, int nch, int* pe, double* ps, unsigned* flags,
-                        hipStream_t st) {
+// With qout (accu), the block-quantized bound input of every line up to nlines_pad is written
+// too (zeros past nlines), in the operand tile layout of q_pad columns.
+static void stats_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, int nch, int* pe, double* ps,
+                        unsigned* flags, int8_t* qout, hipStream_t st) {
   if (nch == 0 || nlines == 0) return;
+  const int ngrid = qout != nullptr ? nlines_pad : nlines;
   if (o.contig) {
-    dim3 grid(nlines, blocks_for(nch, 4 * kColBlocks));
-    hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps, flags);
+    dim3 grid(ngrid, blocks_for(nch, 4 * kColBlocks));
+    hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps, flags,
+                       qout, q_pad);
   } else {
-    dim3 grid(blocks_for(nlines, kWave * kStatsRowGroups), nch);
+    dim3 grid(blocks_for(ngrid, kWave * kStatsRowGroups), nch);
     hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(kStatsThreads), 0, st, o.ptr, o.ld, nlines, q, nch, pe,
-                       ps, flags);
+                       ps, flags, qout, q_pad);
   }
 }
 
 template <bool MAXONLY>
 static hipError_t launch_stats(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
-  stats_lines<MAXONLY>(a, w.p, w.q, w.nch, w.part_e_a, w.part_s_a, w.flags, st);
-  stats_lines<MAXONLY>(b, w.r, w.q, w.nch, w.part_e_b, w.part_s_b, w.flags, st);
+  int8_t* const qa = MAXONLY ? w.abar : nullptr;
+  int8_t* const qb = MAXONLY ? w.bbar : nullptr;
+  stats_lines<MAXONLY>(a, w.p, w.p_pad, w.q, w.q_pad, w.nch, w.part_e_a, w.part_s_a, w.flags, qa, st);
+  stats_lines<MAXONLY>(b, w.r, w.r_pad, w.q, w.q_pad, w.nch, w.part_e_b, w.part_s_b, w.flags, qb, st);
   return hipGetLastError();
+}
+
+static void requant_lines(int8_t* plane, int nlines, int nch, int q_pad, const int* e_line, const int* part_e,
+                          hipStream_t st) {
+  if (nch == 0 || nlines == 0) return;
+  hipLaunchKernelGGL(requant_kernel, dim3(blocks_for(4L * nlines, 256), 4 * nch), dim3(256), 0, st, plane, nlines,
+                     nch, q_pad, e_line, part_e);
 }
 
 hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
@@ -337,27 +390,14 @@ hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w
   return hipGetLastError();
 }
 
-// accu quantized operand plane of one operand (nlines_pad rows, tile-contiguous layout)
-static void quant_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, const int* e, int8_t* out,
-                        hipStream_t st) {
-  if (q_pad == 0) return;
-  if (o.contig) {
-    dim3 grid(nlines_pad / 16, q_pad / kKPad);
-    hipLaunchKernelGGL(quant_cols_kernel, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, q_pad, e, out);
-  } else {
-    dim3 grid(nlines_pad / 64, q_pad / kStageK);
-    hipLaunchKernelGGL(quant_rows_kernel, grid, dim3(256), 0, st, o.ptr, o.ld, nlines, q, q_pad, e, out);
-  }
-}
-
 hipError_t launch_accu_bound_inputs(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
   hipError_t e = launch_stats<true>(a, b, w, st);
   if (e != hipSuccess) return e;
   const int n = w.p + w.r;
   hipLaunchKernelGGL(max_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.nch,
                      w.part_e_a, w.part_e_b, w.e_row, w.f_col);
-  quant_lines(a, w.p, w.p_pad, w.q, w.q_pad, w.e_row, w.abar, st);
-  quant_lines(b, w.r, w.r_pad, w.q, w.q_pad, w.f_col, w.bbar, st);
+  requant_lines(w.abar, w.p, w.nch, w.q_pad, w.e_row, w.part_e_a, st);
+  requant_lines(w.bbar, w.r, w.nch, w.q_pad, w.f_col, w.part_e_b, st);
   // the bound GEMM accumulates maxima with atomics: start from 0
   if ((e = launch_fill_i32(w.rho, 0, w.p, st)) != hipSuccess) return e;
   if ((e = launch_fill_i32(w.gamma, 0, w.r, st)) != hipSuccess) return e;
