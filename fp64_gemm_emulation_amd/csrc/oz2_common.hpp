@@ -48,13 +48,12 @@ __device__ __forceinline__ bool is_nonfinite(double x) {
   return ((bits >> 52) & 0x7FFu) == 0x7FFu;
 }
 
-// ceil(|x| * 2^k) for finite x, exactly, as a double (k may be any integer).
-// If E(x) + k <= 0 the scaled value lies in (0, 1] and the ceiling is 1; otherwise the
-// scaled value is a normal number >= 1 and ldexp is exact.
-__device__ __forceinline__ double ceil_scaled_abs(double x, int ex, int k) {
-  if (x == 0.0) return 0.0;
-  if (ex + k <= 0) return 1.0;
-  return ceil(ldexp(fabs(x), k));
+// ceil(|x| * 2^k) for finite x, exactly, as a double (k may be any integer), without
+// branches: if the scaled value is at least 1 it is a normal number and ldexp is exact;
+// if it lies in (0, 1) its ceiling is 1, which the max supplies even where ldexp rounds
+// it into the subnormal range or to 0; x = 0 gives 0.
+__device__ __forceinline__ double ceil_scaled_abs(double x, int k) {
+  return fmax(ceil(ldexp(fabs(x), k)), x != 0.0 ? 1.0 : 0.0);
 }
 
 // ceil(v / 2^sh) for an exact nonnegative integer v < 2^53 held in a double, sh >= 0.

@@ -91,8 +91,8 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
       for (int L = 0; L < 16; ++L) {
         uint32_t q0 = 0, q1 = 0;
         if (ec != kNoExp) {
-          q0 = static_cast<uint32_t>(ceil_scaled_abs(v[L], exponent_of(v[L]), kQBits - ec));
-          q1 = static_cast<uint32_t>(ceil_scaled_abs(v[L + 16], exponent_of(v[L + 16]), kQBits - ec));
+          q0 = static_cast<uint32_t>(ceil_scaled_abs(v[L], kQBits - ec));
+          q1 = static_cast<uint32_t>(ceil_scaled_abs(v[L + 16], kQBits - ec));
         }
         sq[lane][L][w] = static_cast<uint16_t>(q0 | (q1 << 8));
       }
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
     if (ec != kNoExp) {
 #pragma unroll
       for (int k = 0; k < kStatsCols; ++k) {
-        const double u = ceil_scaled_abs(v[k], exponent_of(v[k]), kFBits - ec);
+        const double u = ceil_scaled_abs(v[k], kFBits - ec);
         acc = fma(u, u, acc);
       }
     }
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
         if (ec != kNoExp) {
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            pk |= static_cast<uint32_t>(ceil_scaled_abs(v[b][k], exponent_of(v[b][k]), kQBits - ec)) << (8 * k);
+            pk |= static_cast<uint32_t>(ceil_scaled_abs(v[b][k], kQBits - ec)) << (8 * k);
         }
         const int L = lane & 15;
         const uint32_t g0 = static_cast<uint32_t>(__shfl(static_cast<int>(pk), L, kWave));
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
       if (ec != kNoExp) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const double u = ceil_scaled_abs(v[b][k], exponent_of(v[b][k]), kFBits - ec);
+          const double u = ceil_scaled_abs(v[b][k], kFBits - ec);
           acc = fma(u, u, acc);
         }
       }
