@@ -100,7 +100,8 @@ __device__ __forceinline__ int residue_byte(const ScaledDigits& g, const DigitCo
   if constexpr (m == 256) {
     return g.lo;  // low byte of A' in two's complement
   } else {
-    // z = lo + sum_k d_k rho_m(2^(22 + 8 k)) = A' (mod m), |z| < 2^22 + 8 * 128 * 127 < 2^23
+    // z = lo + sum_k d_k rho_m(2^(22 + 8 k)) = A' (mod m), |z| < 2^22 + 8 * 128 * 127 < 2^23.
+    // The clamp flag (saturation, never reached at this size) keeps the three-operand form.
     int z = __builtin_amdgcn_sdot4(static_cast<int>(g.w0), cf.c[T][0], g.lo, true);
     if constexpr (ND > 1) z = __builtin_amdgcn_sdot4(static_cast<int>(g.w1), cf.c[T][1], z, true);
     // y = 1.5 * 2^23 + round(z / m): |z| < 2^23, so z / m is within 1/(2m) of z * inv

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
       // block-quantized bound input ceil(|a| 2^(kQBits - e_c)) in the operand tile layout:
       // element 32 w + k of the block goes to chunk slot k mod 16, byte 2 w + k / 16
       static_assert(kStatsColGroups == 8 && kStatsRowGroups == 1, "one row group, two bytes per wave and slot");
-      __shared__ uint16_t sq[kWave][16][8];
+      __shared__ __attribute__((aligned(16))) uint16_t sq[kWave][16][8];  // read as 16-byte chunks
 #pragma unroll
       for (int L = 0; L < 16; ++L) {
         uint32_t q0 = 0, q1 = 0;
