@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 from fp64_gemm_emulation_amd.workloads import generate
-from tests.gpu_helpers import assert_chat_close, assert_equal, chat_tolerance, log, to_device, x_limbs_to_int
+from tests.gpu_helpers import (assert_chat_close, assert_correctly_rounded, assert_equal, chat_tolerance, log, to_device,
+                               x_limbs_to_int)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +50,7 @@ def test_transposed_operands(oz, mode, ta, tb):
     assert_equal(c_ex, c_plain, "ozaki2_dgemm_ex vs ozaki2_dgemm on op(A), op(B)")
     ref = oracle.ozaki2(opA, opB, s, mode)
     assert_chat_close(c_ex, ref["C"], chat_tolerance(opA, opB, np.arange(p), np.arange(r)), "C")
+    assert_correctly_rounded(c_ex, ref["C"], "C")
     log(f"[ex] ok ({int(np.sum(c_ex != ref['C']))} entries differ from the correctly rounded value)")
 
 

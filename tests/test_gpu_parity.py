@@ -70,6 +70,35 @@ def test_edge_values(oz, mode):
     _full_case(oz, A, B, 14, mode, "edges")
 
 
+def _block_spread(rows, q, seed):
+    """rows x q with every 256-long block of a line at its own scale: exponent gaps to the
+    line maximum of 0, 3, 7, 9 and about 1000, an all-zero block, a block of subnormals,
+    and the line maximum sometimes in the short last block."""
+    rng = np.random.default_rng(seed)
+    X = generate(rows, q, 0.5, seed)
+    nblk = (q + 255) // 256
+    shifts = [0, -3, -7, -9, -1000, None, -1060]
+    for i in range(rows):
+        order = rng.permutation(len(shifts))[:nblk]
+        for b in range(nblk):
+            sh = shifts[order[b]]
+            sl = slice(256 * b, min(256 * (b + 1), q))
+            if sh is None:
+                X[i, sl] = 0.0
+            else:
+                X[i, sl] = np.ldexp(X[i, sl], sh)
+    return X
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_block_exponent_spread(oz, mode):
+    """Blocks of one line far apart in scale: the block exponents, the accu bound inputs
+    formed from them, and every later stage, bit-exact against the oracle."""
+    A = _block_spread(70, 1100, 61)
+    B = _block_spread(33, 1100, 62).T.copy()
+    _full_case(oz, A, B, 14, mode, "block spread")
+
+
 @pytest.mark.parametrize("mode", ["fast", "accu"])
 def test_small_integers_exact(oz, mode):
     rng = np.random.default_rng(3)
