@@ -133,28 +133,28 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
 }
 
 // Contiguous lines (columns of B, or rows of op(A) = A^T): one wave per line j and
-// kColBlocks consecutive blocks c; for each block, lane reads l = c kChunk + lane + 64 k,
+// CB consecutive blocks c; for each block, lane reads l = c kChunk + lane + 64 k,
 // k = 0..3, so every load instruction is 512 contiguous bytes, and all of the wave's loads
-// are issued before the first block is reduced.  (One wave per block made 65536 tiny
-// workgroups at n = 8192, which the dispatcher could not launch fast enough.)
-constexpr int kColBlocks = 8;
-template <bool MAXONLY>
+// are issued before the first block is reduced.  CB = 2 where lines have at most 32
+// blocks (more waves in flight on small grids), else 8 (one wave per block made 65536 tiny
+// workgroups at n = 8192, which the dispatcher could not launch fast enough).
+template <bool MAXONLY, int CB>
 __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                          int nch, int* __restrict__ part_e,
                                                          double* __restrict__ part_s,
                                                          unsigned* __restrict__ flags,
                                                          int8_t* __restrict__ qout, int q_pad) {
-  // grid: x = column j, y = groups of 4 kColBlocks blocks; one wave per (j, kColBlocks blocks)
+  // grid: x = column j, y = groups of 4 CB blocks; one wave per (j, CB blocks)
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x;
-  const int c0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kColBlocks;
+  const int c0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * CB;
   if (c0 >= nch) return;  // whole wave
   const bool col_ok = j < r;  // columns up to the padded count when the bound input is written
   const double* col = B + static_cast<long>(col_ok ? j : 0) * ldb;
-  double v[kColBlocks][4];
+  double v[CB][4];
   bool bad = false;
 #pragma unroll
-  for (int b = 0; b < kColBlocks; ++b)
+  for (int b = 0; b < CB; ++b)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int l = (c0 + b) * kChunk + lane + kWave * k;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
     }
   if (bad) atomicOr(flags, kFlagNonFinite);
 #pragma unroll
-  for (int b = 0; b < kColBlocks; ++b) {
+  for (int b = 0; b < CB; ++b) {
     const int c = c0 + b;
     if (c >= nch) break;  // whole wave
     int emax = kNoExp;
@@ -355,9 +355,15 @@ static void stats_lines(const Operand& o, int nlines, int nlines_pad, int q, int
   if (nch == 0 || nlines == 0) return;
   const int ngrid = qout != nullptr ? nlines_pad : nlines;
   if (o.contig) {
-    dim3 grid(ngrid, blocks_for(nch, 4 * kColBlocks));
-    hipLaunchKernelGGL(stats_cols_kernel<MAXONLY>, grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps, flags,
-                       qout, q_pad);
+    if (nch <= 32) {
+      dim3 grid(ngrid, blocks_for(nch, 4 * 2));
+      hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 2>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps,
+                         flags, qout, q_pad);
+    } else {
+      dim3 grid(ngrid, blocks_for(nch, 4 * 8));
+      hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 8>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps,
+                         flags, qout, q_pad);
+    }
   } else {
     dim3 grid(blocks_for(ngrid, kWave * kStatsRowGroups), nch);
     hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(kStatsThreads), 0, st, o.ptr, o.ld, nlines, q, nch, pe,
