@@ -158,6 +158,27 @@ def test_deterministic_and_leading_dimensions(oz):
     assert not Cbig[200:, :].any()
 
 
+def test_runs_on_the_callers_stream(oz):
+    """A call on a side stream (default priority), with stage timing on, gives the same C
+    as one on the default stream, and its timing events are recorded on that stream."""
+    import torch
+    A = generate(300, 700, 0.5, 17)
+    B = generate(700, 260, 0.5, 18)
+    Ad, Bd = to_device(A), to_device(B)
+    c_default = oz.dgemm(Ad, Bd, 14, "fast")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert oz.ozaki2_timing_begin(2) == oz.OZ2_OK
+        c_side = oz.empty_colmajor(300, 260)
+        for _ in range(2):
+            oz.dgemm(Ad, Bd, 14, "fast", out=c_side, stream=side)
+    side.synchronize()
+    rc, stage_ms, ncalls = oz.ozaki2_timing_end()
+    assert rc == oz.OZ2_OK and ncalls == 2 and all(t > 0.0 for t in stage_ms)
+    assert torch.equal(c_side, c_default)
+
+
 def test_caller_workspace_and_timing(oz):
     import torch
     A = generate(128, 256, 0.5, 1)
