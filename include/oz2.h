@@ -31,6 +31,10 @@
  *     has been launched and C is untouched.
  *   - Not thread-safe: calls share one library workspace and one timing state; calls on
  *     different streams that share a workspace must be ordered by the caller.
+ *   - ozaki2_dgemm and ozaki2_dgemm_ex enqueue kernels only (no allocation, memory set or
+ *     copy) once their workspace exists, so a call can be captured in a HIP graph when a
+ *     caller workspace is set (or an earlier call of the same or larger size has created
+ *     the library's); the graph keeps the workspace pointer, which must stay valid.
  */
 #ifndef OZ2_H
 #define OZ2_H

@@ -179,6 +179,44 @@ def test_runs_on_the_callers_stream(oz):
     assert torch.equal(c_side, c_default)
 
 
+def test_graph_capture_replays(oz):
+    """One call captured into a graph (caller workspace, so nothing is allocated inside the
+    capture) and replayed four times, with eager calls and synchronizations in between;
+    every replay must give the eager result."""
+    import torch
+    p, q, r, s = 300, 517, 200, 14
+    A = generate(p, q, 0.5, 71)
+    B = generate(q, r, 0.5, 72)
+    Ad, Bd = to_device(A), to_device(B)
+    need = oz.ozaki2_workspace_size(p, q, r, s, oz.OZ2_FAST)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    base = (ws.data_ptr() + 255) // 256 * 256
+    assert oz.ozaki2_set_workspace(base, need) == oz.OZ2_OK
+    try:
+        side = torch.cuda.Stream()
+        C = oz.empty_colmajor(p, r)
+        with torch.cuda.stream(side):
+            oz.dgemm(Ad, Bd, s, "fast", out=C, stream=side)
+        side.synchronize()
+        want = C.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            oz.dgemm(Ad, Bd, s, "fast", out=C, stream=side)
+        for k in range(4):
+            C.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(C, want), f"replay {k}"
+            other = oz.dgemm(Ad, Bd, s, "fast")           # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(other, want)
+        del graph
+        torch.cuda.synchronize()
+    finally:
+        assert oz.ozaki2_set_workspace(None, 0) == oz.OZ2_OK
+
+
 def test_caller_workspace_and_timing(oz):
     import torch
     A = generate(128, 256, 0.5, 1)
