@@ -51,6 +51,7 @@ def _load():
         "ozaki2_release": (i, []),
         "ozaki2_timing_begin": (i, [i]),
         "ozaki2_timing_end": (i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i)]),
+        "ozaki2_get_stage_ms": (i, [ctypes.POINTER(ctypes.c_float)]),
         "ozaki2_get_flags": (i, [ctypes.POINTER(ctypes.c_uint)]),
         "ozaki2_moduli": (i, [i, ctypes.POINTER(i)]),
         "ozaki2_tau": (i, [i]),
@@ -102,6 +103,13 @@ def ozaki2_timing_end():
     n = ctypes.c_int(0)
     rc = _LIB.ozaki2_timing_end(ms, ctypes.byref(n))
     return rc, list(ms), n.value
+
+
+def ozaki2_get_stage_ms():
+    """Returns (status, [scaling, residues, gemm, crt] ms of the most recent timed call)."""
+    ms = (ctypes.c_float * 4)()
+    rc = _LIB.ozaki2_get_stage_ms(ms)
+    return rc, list(ms)
 
 
 def ozaki2_get_flags():

@@ -180,6 +180,7 @@ struct State {
   bool timing = false;
   int timing_max = 0;
   int timing_n = 0;
+  int last_timed = -1;  // event set of the most recent timed call
   std::vector<hipEvent_t> events;  // 5 per timed call
   // last call (for flags)
   hipStream_t last_stream = nullptr;
@@ -223,6 +224,7 @@ struct Recorder {
   explicit Recorder(hipStream_t s) : st(s) {
     if (g.timing && g.timing_n < g.timing_max) {
       ev = &g.events[5 * static_cast<size_t>(g.timing_n)];
+      g.last_timed = g.timing_n;
       ++g.timing_n;
     }
   }
@@ -363,6 +365,7 @@ int ozaki2_release(void) {
   g.events.clear();
   g.timing = false;
   g.timing_max = g.timing_n = 0;
+  g.last_timed = -1;
   g.last_flags = nullptr;
   g.last_stream = nullptr;
   return rc;
@@ -400,6 +403,16 @@ int ozaki2_timing_end(double* stage_ms, int* ncalls) {
     }
   }
   g.timing_n = 0;
+  return OZ2_OK;
+}
+
+int ozaki2_get_stage_ms(float* ms) {
+  if (ms == nullptr || g.last_timed < 0 || 5 * static_cast<size_t>(g.last_timed) + 4 >= g.events.size())
+    return OZ2_ERR_ARG;
+  hipEvent_t* ev = &g.events[5 * static_cast<size_t>(g.last_timed)];
+  if (hipEventSynchronize(ev[4]) != hipSuccess) return OZ2_ERR_HIP;
+  for (int k = 0; k < 4; ++k)
+    if (hipEventElapsedTime(&ms[k], ev[k], ev[k + 1]) != hipSuccess) return OZ2_ERR_HIP;
   return OZ2_OK;
 }
 

@@ -182,6 +182,12 @@ int ozaki2_dgemm_debug(int p, int q, int r, const double* A, int lda, const doub
 int ozaki2_timing_begin(int max_calls);
 int ozaki2_timing_end(double* stage_ms, int* ncalls);
 
+/* The four stage times in milliseconds (same order as above) of the most recent call that
+ * was timed (made while ozaki2_timing_begin was in effect; untimed calls record no events).
+ * Synchronizes on that call's last event.  OZ2_ERR_ARG if ms is NULL or no call has been
+ * timed since the library's events were created, OZ2_ERR_HIP on a runtime error. */
+int ozaki2_get_stage_ms(float* ms);
+
 /* Synchronizes the stream of the last call and returns its flag word (OZ2_FLAG_*). */
 int ozaki2_get_flags(unsigned* flags);
 

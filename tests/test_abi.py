@@ -159,3 +159,11 @@ def test_tensor_wrappers_reject_bad_operands_before_the_library(lib):
         lib.dgemm_ex(a, b, beta=1.0)
     with pytest.raises(ValueError, match="wrong shape"):
         lib.dgemm_ex(a, b, C=torch.zeros(4, 4, dtype=torch.float64))
+
+
+def test_stage_times_need_a_timed_call(lib):
+    """ozaki2_get_stage_ms answers on the host when there is nothing to report."""
+    import ctypes as ct
+    assert lib._LIB.ozaki2_get_stage_ms(None) == lib.OZ2_ERR_ARG
+    rc, _ = lib.ozaki2_get_stage_ms()
+    assert rc == lib.OZ2_ERR_ARG          # no call has been timed in this process

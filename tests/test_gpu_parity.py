@@ -174,8 +174,11 @@ def test_runs_on_the_callers_stream(oz):
         for _ in range(2):
             oz.dgemm(Ad, Bd, 14, "fast", out=c_side, stream=side)
     side.synchronize()
+    rc, last_ms = oz.ozaki2_get_stage_ms()
+    assert rc == oz.OZ2_OK and all(t > 0.0 for t in last_ms)
     rc, stage_ms, ncalls = oz.ozaki2_timing_end()
     assert rc == oz.OZ2_OK and ncalls == 2 and all(t > 0.0 for t in stage_ms)
+    assert all(a <= b + 1e-3 for a, b in zip(last_ms, stage_ms))   # one call's stages within the two-call sums
     assert torch.equal(c_side, c_default)
 
 
