@@ -56,6 +56,20 @@ def test_every_modulus_count(oz, mode, s):
     _full_case(oz, A, B, s, mode, f"s{s}")
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_random_small_shapes(oz, case):
+    """Seeded random shapes (each dimension 1..399), moduli counts, modes and exponent
+    spreads, every intermediate compared."""
+    rng = np.random.default_rng(9000 + case)
+    p, q, r = (int(x) for x in rng.integers(1, 400, size=3))
+    s = int(rng.integers(2, 21))
+    mode = ("fast", "accu")[case % 2]
+    phi = float(rng.choice([0.5, 1.0, 2.0]))
+    A = generate(p, q, phi, 9100 + case)
+    B = generate(q, r, phi, 9200 + case)
+    _full_case(oz, A, B, s, mode, f"random {case} phi={phi}")
+
+
 @pytest.mark.parametrize("mode", ["fast", "accu"])
 def test_edge_values(oz, mode):
     A = generate(64, 300, 4.0, 5)          # very wide exponent spread
