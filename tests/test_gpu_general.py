@@ -181,18 +181,19 @@ def test_accu_bound_product_at_its_int32_limit(oz):
     assert_chat_close(out["C"].cpu().numpy(), ref["C"], chat_tolerance(A, B, np.arange(p), np.arange(r)), "C")
 
 
+@pytest.mark.parametrize("mode", ["fast", "accu"])
 @pytest.mark.parametrize("shape", [(1 << 23, 5, 3), (3, 5, 1 << 23)])
-def test_max_rows_or_columns(oz, shape):
+def test_max_rows_or_columns(oz, shape, mode):
     """p or r at the largest accepted size, 2^23 (the launch grids at their widest)."""
     p, q, r = shape
     s = 2
     A = generate(p, q, 0.5, 83)
     B = generate(q, r, 0.5, 84)
-    log(f"[max dim] p,q,r={p},{q},{r} s={s}")
-    out = oz.dgemm_debug(to_device(A), to_device(B), s, "fast", want=("d", "b"))
+    log(f"[max dim] p,q,r={p},{q},{r} s={s} mode={mode}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=("d", "b"))
     rows = np.array(sorted({0, 1, p // 2, p - 2, p - 1}))
     cols = np.array(sorted({0, 1, r // 2, r - 2, r - 1}))
-    ref = oracle.ozaki2_sample(A, B, s, "fast", rows, cols)
+    ref = oracle.ozaki2_sample(A, B, s, mode, rows, cols)
     import torch
     assert_equal(out["d"][torch.as_tensor(rows, device="cuda")].cpu().numpy(), ref["d"].astype(np.int32), "d")
     assert_equal(out["b"][torch.as_tensor(cols, device="cuda")].cpu().numpy(), ref["b"].astype(np.int32), "b")
