@@ -137,7 +137,8 @@ int ozaki2_release(void);
  *   Bt[s*r*q]            B_t[l][j] at Bt[(t*r + j)*q + l]
  *   P[s*r*p]             P_t[i][j] at P[(t*r + j)*p + i]   (int32; only for q <= OZ2_MAX_Q_P_DUMP)
  *   R[s*r*p]             R_t[i][j] at R[(t*r + j)*p + i]   (uint8)
- *   X[r*p*5]             X[i][j] at X[(j*p + i)*5 + k], k = 0..4 little-endian limbs
+ *   X[r*p*5]             X[i][j] at X[(j*p + i)*5 + k], k = 0..4: the 32-bit words of X as a
+ *                        160-bit two's-complement integer, least significant first
  * accu mode only (ignored in fast mode):
  *   e[p], f[r]           max-abs exponents of rows of A / columns of B (E(x): 2^(E-1) <= |x| < 2^E;
  *                        INT32_MIN for an all-zero line)
