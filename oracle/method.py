@@ -48,12 +48,14 @@ design notes of the repository):
 Pins (tests/test_oracle_pins.py): moduli, M and tau against the pages' range
 figures; residues against their definition by brute force and against the
 split-integer route of [P] section 10.1; products and X = A'B' against Python
-integer brute force; scalings against exact rational soundness bounds and
-Eq. 18 of [S] section 2; C_hat against exact products and closed forms.
-Parity unpinned: the exact fast/accu exponent *rule* is this oracle's reading
-(the pages give no formula), so its agreement with any other implementation's
-exponent choice is not pinned; only its soundness (|A'B'| <= 2^tau) and, for
-fast, its near-maximality are.
+integer brute force; scalings against exact rational soundness bounds, and the
+exponents of both modes against Eq. 18 of [S] section 2 on flat lines (where the
+equal budget is the exact exponent) and against maximality under the equal
+split (accu: bound product and maxima by Python-int brute force); C_hat against
+exact products and closed forms.  The exponent rule away from flat lines is this
+oracle's reading (the pages give no formula), so its agreement with another
+implementation's choice there is not pinned; its value on flat lines, its
+soundness and its maximality are.
 """
 from __future__ import annotations
 
@@ -255,7 +257,13 @@ def accu_bound_inputs(rows: np.ndarray):
 
 
 def _accu_d(e_list, peaks, s: int) -> np.ndarray:
-    """d = floor((tau - clog2(max(peak, 1))) / 2) + Q - e; zero line -> 0."""
+    """d = floor((tau - clog2(max(peak, 1))) / 2) + Q - e; zero line -> 0.
+
+    The largest integer with 4^(d + e - Q) 2^clog2(peak) <= 2^tau: the budget split
+    equally through Y_ij <= sqrt(rho_i gamma_j).  A nonzero line whose peak is 0 (every
+    one of its bound products vanishes, so its outputs are exactly 0) is scaled as a
+    line of peak 1, which keeps its |A'| below 2^(floor(tau/2) + Q) like every other line.
+    """
     t = tau(s)
     d = np.zeros(len(e_list), dtype=np.int64)
     for i, (ei, pk) in enumerate(zip(e_list, peaks)):

@@ -84,6 +84,27 @@ def test_edge_values(oz, mode):
     _full_case(oz, A, B, 14, mode, "edges")
 
 
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_lines_whose_products_all_vanish(oz, mode):
+    """A nonzero row of A supported only on zero rows of B (accu: bound peak rho = 0) and a
+    nonzero column of B supported only on zero columns of A (gamma = 0): the exponents of
+    such lines (scaled as lines of peak 1 in accu), their truncations and residues, and
+    their exactly zero outputs, bit-exact against the oracle."""
+    A = generate(70, 300, 1.0, 41)
+    B = generate(300, 45, 1.0, 42)
+    A[:, 40:48] = 0.0
+    B[:, 9] = 0.0
+    B[40:48, 9] = generate(8, 1, 3.0, 43)[:, 0] * 1e150     # column 9 of B meets only zero columns of A
+    B[200:203, :] = 0.0
+    A[17, :] = 0.0
+    A[17, 200:203] = [-3e-250, 1e-249, 7e-251]              # row 17 of A meets only zero rows of B
+    out, ref = _full_case(oz, A, B, 14, mode, "vanishing lines")
+    if mode == "accu":
+        assert int(ref["rho"][17]) == 0 and int(ref["gamma"][9]) == 0
+    c = out["C"].cpu().numpy()
+    assert not c[17, :].any() and not c[:, 9].any()
+
+
 def _block_spread(rows, q, seed):
     """rows x q with every 256-long block of a line at its own scale: exponent gaps to the
     line maximum of 0, 3, 7, 9 and about 1000, an all-zero block, a block of subnormals,

@@ -13,7 +13,7 @@ from tests import test_oracle_pins as pins
 
 _orig = {name: getattr(oz, name) for name in
          ["centered_residue", "crt", "scale_truncate", "fast_exponents",
-          "accu_bound_inputs", "residue_product", "inverse_scale", "moduli"]}
+          "accu_bound_inputs", "_accu_d", "residue_product", "inverse_scale", "moduli"]}
 
 
 def _nonneg_residue(xp, m):
@@ -56,6 +56,21 @@ def _accu_round_down(rows):
     return e, out
 
 
+def _accu_d_plus_one(e_list, peaks, s):
+    d = _orig["_accu_d"](e_list, peaks, s)
+    return np.where(np.array([x is not None for x in e_list], dtype=bool), d + 1, d)
+
+
+def _accu_d_minus_one(e_list, peaks, s):
+    d = _orig["_accu_d"](e_list, peaks, s)
+    return np.where(np.array([x is not None for x in e_list], dtype=bool), d - 1, d)
+
+
+def _accu_d_zero_peak_unscaled(e_list, peaks, s):
+    d = _orig["_accu_d"](e_list, peaks, s)
+    return np.where(np.asarray(peaks, dtype=np.int64) == 0, 0, d)
+
+
 def _product_reversed_k(at, bt):
     return _orig["residue_product"](np.asarray(at)[:, ::-1], bt)
 
@@ -72,6 +87,11 @@ CASES = [
     ("fast_exponents", _fast_plus_one, lambda g: pins.test_fast_exponent_sound_and_near_maximal(14)),
     ("fast_exponents", _fast_minus_one, lambda g: pins.test_fast_exponent_sound_and_near_maximal(14)),
     ("accu_bound_inputs", _accu_round_down, lambda g: pins.test_accu_bound_inputs_round_upward(14)),
+    ("_accu_d", _accu_d_plus_one, lambda g: pins.test_eq18_equal_budget_on_flat_lines_accu()),
+    ("_accu_d", _accu_d_minus_one, lambda g: pins.test_eq18_equal_budget_on_flat_lines_accu()),
+    ("_accu_d", _accu_d_plus_one, lambda g: pins.test_accu_exponent_maximal_against_bruteforce(14)),
+    ("_accu_d", _accu_d_minus_one, lambda g: pins.test_accu_exponent_maximal_against_bruteforce(14)),
+    ("_accu_d", _accu_d_zero_peak_unscaled, lambda g: pins.test_accu_nonzero_line_with_zero_bound_peak(14)),
     ("residue_product", _product_reversed_k, lambda g: pins.test_residue_product_bruteforce()),
     ("inverse_scale", _inverse_scale_wrong_sign,
      lambda g: pins.test_small_integer_inputs_give_exact_product("fast", 14)),
@@ -81,7 +101,8 @@ CASES = [
 @pytest.mark.parametrize("name,wrong,pin", CASES, ids=[f"{c[0]}-{c[1].__name__}" for c in CASES])
 def test_planted_mistake_is_caught(monkeypatch, golden_dir, name, wrong, pin):
     monkeypatch.setattr(oz, name, wrong)
-    monkeypatch.setattr(oracle, name, wrong)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, wrong)
     with pytest.raises(Exception):
         pin(golden_dir)
 

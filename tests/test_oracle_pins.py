@@ -273,6 +273,107 @@ def test_accu_bound_inputs_round_upward(s):
             assert q_il - 1 < exact <= q_il
 
 
+def test_eq18_equal_budget_on_flat_lines_accu():
+    """All-ones 1 x q A and q x 1 B: accu d and b both equal Eq. 18's k.
+
+    Ozaki II supplement section 2, Eq. 18: with |a'| <= 2^k and |b'| <= 2^k the
+    product is bounded by q 2^(2k), and the equal budget is the largest k with
+    q 4^k <= M/2 - 1.  For lines of ones the bound product is the exact product,
+    so the accu exponents must be exactly that k (the fast mode's counterpart is
+    test_eq18_equal_budget_on_flat_rows).
+    """
+    for s in (2, 8, 14, 18, 20):
+        M = oracle.modulus_product(s)
+        for j in range(0, 13):
+            q = 1 << j
+            k = 0
+            while q * 4 ** (k + 1) <= M // 2 - 1:
+                k += 1
+            assert q * 4 ** k <= M // 2 - 1 < q * 4 ** (k + 1)
+            out = oracle.accu_exponents(np.ones((1, q)), np.ones((q, 1)), s)
+            assert int(out["d"][0]) == k and int(out["b"][0]) == k, (s, q)
+
+
+def _pow2_at_least(v):
+    """Smallest power of two >= v (v >= 1), by doubling."""
+    p = 1
+    while p < v:
+        p *= 2
+    return p
+
+
+@pytest.mark.parametrize("s", [2, 8, 14, 18, 20])
+def test_accu_exponent_maximal_against_bruteforce(s):
+    """Bound product and its maxima by Python-int loops; d and b are the largest
+    integers whose squared scale times the bound peak (rounded up to a power of two,
+    so the equal split stays an integer exponent) fits the budget 2^tau:
+      4^(d + e - Q) P2(rho) <= 2^tau < 4^(d + 1 + e - Q) P2(rho).
+    The upward-quantized inputs are rebuilt here from exact Fractions."""
+    t = oracle.tau(s)
+    Q = oracle.Q_BITS
+    A = generate(6, 37, 2.0, 300 + s)
+    B = generate(37, 5, 2.0, 400 + s)
+    A[4, :] = 0.0                        # zero row: d = 0
+    out = oracle.accu_exponents(A, B, s)
+
+    def quantize(line):
+        mx = max(abs(Fraction(float(v))) for v in line)
+        if mx == 0:
+            return None, [0] * len(line)
+        e = 0
+        while Fraction(2) ** e <= mx:
+            e += 1
+        while Fraction(2) ** (e - 1) > mx:
+            e -= 1
+        qs = []
+        for v in line:
+            x = abs(Fraction(float(v))) * Fraction(2) ** (Q - e)
+            qs.append(-((-x.numerator) // x.denominator))   # exact ceiling
+        return e, qs
+
+    rows = [quantize(A[i, :]) for i in range(A.shape[0])]
+    cols = [quantize(B[:, j]) for j in range(B.shape[1])]
+    y = [[sum(a * b for a, b in zip(rq, cq)) for (_, cq) in cols] for (_, rq) in rows]
+    for lines, peaks, exps in ((rows, [max(r) for r in y], out["d"]),
+                               (cols, [max(y[i][j] for i in range(len(rows))) for j in range(len(cols))], out["b"])):
+        for (e, _), peak, d in zip(lines, peaks, exps):
+            d = int(d)
+            if e is None:
+                assert d == 0
+                continue
+            assert peak >= 1
+            p2 = _pow2_at_least(peak)
+            assert Fraction(4) ** (d + e - Q) * p2 <= 2 ** t
+            assert Fraction(4) ** (d + 1 + e - Q) * p2 > 2 ** t
+
+
+@pytest.mark.parametrize("s", [8, 14, 20])
+def test_accu_nonzero_line_with_zero_bound_peak(s):
+    """A nonzero row of A whose products with every column of B vanish (its support
+    meets only zero rows of B) has rho = 0, and likewise a column of B against zero
+    columns of A has gamma = 0.  Reading taken: such a line is scaled as if its peak
+    were 1, d = floor(tau / 2) + Q - e, which keeps |A'| <= 2^(floor(tau/2) + Q) like any
+    line with a nonzero peak; its outputs are exactly 0 whatever its exponent."""
+    t = oracle.tau(s)
+    A = generate(4, 6, 1.0, 7)
+    B = generate(6, 3, 1.0, 8)
+    A[:, 2] = 0.0                        # column 2 of A is zero ...
+    B[:, 1] = 0.0
+    B[2, 1] = 1e200                      # ... so column 1 of B (support {2}) has gamma = 0
+    B[4, :] = 0.0                        # row 4 of B is zero ...
+    A[1, :] = 0.0
+    A[1, 4] = -3e-250                    # ... so row 1 of A (support {4}) has rho = 0
+    out = oracle.accu_exponents(A, B, s)
+    assert int(out["rho"][1]) == 0 and int(out["gamma"][1]) == 0
+    assert int(out["d"][1]) == t // 2 + oracle.Q_BITS - out["e"][1]
+    assert int(out["b"][1]) == t // 2 + oracle.Q_BITS - out["f"][1]
+    full = oracle.ozaki2(A, B, s, "accu")
+    assert np.abs(full["Ap"][1]).max() <= 2.0 ** (t // 2 + oracle.Q_BITS)
+    assert np.abs(full["Bp"][:, 1]).max() <= 2.0 ** (t // 2 + oracle.Q_BITS)
+    assert not full["C"][1, :].any() and not full["C"][:, 1].any()
+    assert all(int(v) == 0 for v in full["X"][1, :]) and all(int(v) == 0 for v in full["X"][:, 1])
+
+
 @pytest.mark.parametrize("s", [2, 8, 14, 18, 20])
 def test_accu_bound_product_and_scaling_sound(s):
     A = generate(5, 40, 1.5, 21 + s)
