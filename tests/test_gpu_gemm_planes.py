@@ -1,0 +1,176 @@
+"""Element-complete parity of the production GEMM (gemm_w8_kernel: 8 waves of
+v_mfma_i32_16x16x64_i8, 256 x 256 tiles), which runs whenever a launch has at least 512
+tiles of 256 x 256 over all its planes.  Every element of the compared R_t planes must
+equal the oracle's R_t = (A_t B_t) mod m_t ("Ozaki II supplement", section 1.1: with
+2 c_max < M the CRT of these residues is X = A'B' exactly), so a slip confined to one
+lane, register or tile position cannot hide between samples.
+
+The oracle's step functions (exponents, scaled truncation, centered residues, exact
+products, output residues) run in that order on the whole operands; the elementwise ones
+are called on row ranges in threads (NumPy releases the GIL), which changes nothing
+about what they compute.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+from fp64_gemm_emulation_amd.workloads import WORKLOADS, generate
+from tests.gpu_helpers import assert_equal, compare_sampled, log, sample_indices, to_device
+
+pytestmark = pytest.mark.gpu
+
+_THREADS = 8
+
+
+@pytest.fixture(scope="module")
+def oz():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    from fp64_gemm_emulation_amd import binding
+    return binding
+
+
+def _ranges(n, parts):
+    edges = np.linspace(0, n, min(parts, max(n, 1)) + 1).astype(int)
+    return [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+
+def _by_rows(fn, nrows):
+    """fn(lo, hi) over row ranges in threads, results stacked along axis 0."""
+    with ThreadPoolExecutor(_THREADS) as ex:
+        parts = list(ex.map(lambda rg: fn(*rg), _ranges(nrows, 4 * _THREADS)))
+    return np.concatenate(parts, axis=0)
+
+
+def oracle_exponents(A, B, s, mode):
+    """(d, b, extras) from the oracle: fast per line (row ranges in threads), accu whole."""
+    if mode == "accu":
+        out = oracle.accu_exponents(A, B, s)
+        return out["d"], out["b"], out
+    Bt = np.asarray(B).T
+    d = _by_rows(lambda lo, hi: oracle.fast_exponents(A[lo:hi], s)[0], A.shape[0])
+    b = _by_rows(lambda lo, hi: oracle.fast_exponents(Bt[lo:hi], s)[0], Bt.shape[0])
+    return d, b, {}
+
+
+def oracle_planes(A, B, s, d, b, planes):
+    """Yield (t, R_t) for the requested modulus indices, R_t p x r, from the oracle's steps:
+    A' = trunc(2^d A), B' = trunc(B 2^b), centered residues, exact product, mod m_t."""
+    Bt = np.asarray(B).T
+    ap = _by_rows(lambda lo, hi: oracle.scale_truncate(A[lo:hi], d[lo:hi]), A.shape[0])
+    bpt = _by_rows(lambda lo, hi: oracle.scale_truncate(Bt[lo:hi], b[lo:hi]), Bt.shape[0])
+    mods = oracle.moduli(s)
+    for t in planes:
+        m = mods[t]
+        at = _by_rows(lambda lo, hi: oracle.centered_residue(ap[lo:hi], m), ap.shape[0])
+        btt = _by_rows(lambda lo, hi: oracle.centered_residue(bpt[lo:hi], m), bpt.shape[0])
+        yield t, oracle.output_residue(oracle.residue_product(at, btt.T), m), at, btt
+
+
+def big_tiles(p, r, s):
+    return ((p + 255) // 256) * ((r + 255) // 256) * s
+
+
+def _compare_planes(out, A, B, s, d, b, planes, label, operands=False):
+    for t, R, at, btt in oracle_planes(A, B, s, d, b, planes):
+        assert_equal(out["R"][t].cpu().numpy().T, R.astype(np.uint8), f"{label} R_t t={t}")
+        if operands:
+            assert_equal(out["At"][t].cpu().numpy(), at.astype(np.int8), f"{label} A_t t={t}")
+            assert_equal(out["Bt"][t].cpu().numpy(), btt.astype(np.int8), f"{label} B_t t={t}")
+        log(f"[planes] {label}: plane t={t} (m={oracle.moduli(s)[t]}) equal in full")
+
+
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_production_gemm_every_plane_in_full(oz, mode):
+    """p = r = 2048, q = 700, s = 14: 896 tiles, the 8-wave kernel.  Every R_t, A_t and B_t
+    element, d and b (and e, f, rho, gamma in accu) in full; X and C on samples."""
+    import torch
+    p, q, r, s = 2048, 700, 2048, 14
+    assert big_tiles(p, r, s) >= 512
+    A = generate(p, q, 1.0, 501)
+    B = generate(q, r, 1.0, 502)
+    want = ("d", "b", "Ap", "Bp", "At", "Bt", "R", "X") + (("e", "f", "rho", "gamma", "Abar", "Bbar")
+                                                           if mode == "accu" else ())
+    log(f"[planes] production GEMM {mode}: p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=want)
+    torch.cuda.synchronize()
+    d, b, ex = oracle_exponents(A, B, s, mode)
+    assert_equal(out["d"].cpu().numpy(), d.astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), b.astype(np.int32), "b")
+    if mode == "accu":
+        assert_equal(out["rho"].cpu().numpy(), ex["rho"].astype(np.int32), "rho")
+        assert_equal(out["gamma"].cpu().numpy(), ex["gamma"].astype(np.int32), "gamma")
+    _compare_planes(out, A, B, s, d, b, range(s), f"2048x700x2048 {mode}", operands=True)
+    rows = sample_indices(p, 12, 5)
+    cols = sample_indices(r, 12, 6)
+    compare_sampled(out, oracle.ozaki2_sample(A, B, s, mode, rows, cols), A, B, s, mode, rows, cols)
+    log(f"[planes] production GEMM {mode}: ok")
+
+
+def test_headline_workload_planes_in_full(oz):
+    """n = 8192 fast, s = 14: the m = 256 plane and an odd plane (m = 199) in full."""
+    import torch
+    w = WORKLOADS["n8192_fast_s14"]
+    A, B = w.inputs()
+    log(f"[planes] {w.name}: GPU run")
+    out = oz.dgemm_debug(to_device(A), to_device(B), w.s, w.mode, want=("d", "b", "R"))
+    torch.cuda.synchronize()
+    log(f"[planes] {w.name}: oracle exponents")
+    d, b, _ = oracle_exponents(A, B, w.s, w.mode)
+    assert_equal(out["d"].cpu().numpy(), d.astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), b.astype(np.int32), "b")
+    _compare_planes(out, A, B, w.s, d, b, [0, w.s - 1], w.name)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_accu_workload_scalings_in_full(oz):
+    """n = 8192 accu, s = 14 (bound GEMM on the 8-wave kernel with its row / column maximum
+    epilogue): e, f, rho, gamma, d and b in full, and one residue plane (m = 233) in full."""
+    import torch
+    w = WORKLOADS["n8192_accu_s14"]
+    A, B = w.inputs()
+    log(f"[planes] {w.name}: GPU run")
+    assert big_tiles(w.n, w.n, 1) >= 512
+    out = oz.dgemm_debug(to_device(A), to_device(B), w.s, w.mode,
+                         want=("d", "b", "e", "f", "rho", "gamma", "R"))
+    torch.cuda.synchronize()
+    log(f"[planes] {w.name}: oracle bound product")
+    d, b, ex = oracle_exponents(A, B, w.s, w.mode)
+    assert all(v is not None for v in ex["e"]) and all(v is not None for v in ex["f"])
+    assert_equal(out["e"].cpu().numpy(), np.array(ex["e"], dtype=np.int32), "e")
+    assert_equal(out["f"].cpu().numpy(), np.array(ex["f"], dtype=np.int32), "f")
+    assert_equal(out["rho"].cpu().numpy(), ex["rho"].astype(np.int32), "rho")
+    assert_equal(out["gamma"].cpu().numpy(), ex["gamma"].astype(np.int32), "gamma")
+    assert_equal(out["d"].cpu().numpy(), d.astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), b.astype(np.int32), "b")
+    _compare_planes(out, A, B, w.s, d, b, [7], w.name)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_k_blocked_production_gemm_every_plane(oz):
+    """q = 2^17 + 256 (two K-blocks: the second runs the 8-wave kernel's accumulate
+    epilogue, R_t <- (P_block + R_t) mod m_t), p = r = 1281 (ragged last tile row and
+    column), s = 15: 540 tiles.  Every element of every R_t plane; X and C on samples."""
+    import torch
+    p, q, r, s = 1281, (1 << 17) + 256, 1281, 15
+    assert big_tiles(p, r, s) >= 512
+    A = generate(p, q, 0.5, 601)
+    B = generate(q, r, 0.5, 602)
+    log(f"[planes] K-blocked: p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, "fast", want=("d", "b", "Ap", "Bp", "At", "Bt", "R", "X"))
+    torch.cuda.synchronize()
+    d, b, _ = oracle_exponents(A, B, s, "fast")
+    assert_equal(out["d"].cpu().numpy(), d.astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), b.astype(np.int32), "b")
+    _compare_planes(out, A, B, s, d, b, range(s), "K-blocked")
+    rows = np.array(sorted(set(sample_indices(p, 5, 7).tolist()) | {255, 256, 1279, 1280}))
+    cols = np.array(sorted(set(sample_indices(r, 5, 8).tolist()) | {255, 256, 1279, 1280}))
+    compare_sampled(out, oracle.ozaki2_sample(A, B, s, "fast", rows, cols), A, B, s, "fast", rows, cols)
+    log("[planes] K-blocked: ok")
+    del out
+    torch.cuda.empty_cache()
