@@ -20,6 +20,7 @@ OZ2_OK, OZ2_ERR_ARG, OZ2_ERR_UNSUPPORTED, OZ2_ERR_WORKSPACE, OZ2_ERR_HIP = 0, 1,
 OZ2_MIN_S, OZ2_MAX_S, OZ2_MAX_Q, OZ2_MAX_Q_P_DUMP, OZ2_X_LIMBS = 2, 20, 524287, 131071, 5
 OZ2_OP_N, OZ2_OP_T = 0, 1
 OZ2_FLAG_NONFINITE = 1
+OZ2_NOALLOC_SCRATCH_BYTES = 256 << 20
 MODES = {"fast": OZ2_FAST, "accu": OZ2_ACCU}
 
 
@@ -44,6 +45,7 @@ def _load():
     i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     sig = {
         "ozaki2_dgemm": (i, [i, i, i, vp, i, vp, i, vp, i, i, i, vp]),
+        "ozaki2_dgemm_noalloc": (i, [i, i, i, vp, i, vp, i, vp, i, i, i, vp]),
         "ozaki2_dgemm_ex": (i, [i, i, i, i, i, ctypes.c_double, vp, i, vp, i, ctypes.c_double, vp, i, i, i, vp]),
         "ozaki2_dgemm_debug": (i, [i, i, i, vp, i, vp, i, vp, i, i, i, vp, ctypes.POINTER(OZ2Dump)]),
         "ozaki2_workspace_size": (sz, [i, i, i, i, i]),
@@ -70,6 +72,10 @@ _LIB = _load()
 # --- entry points with the C names -------------------------------------------------
 def ozaki2_dgemm(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream) -> int:
     return _LIB.ozaki2_dgemm(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream)
+
+
+def ozaki2_dgemm_noalloc(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream) -> int:
+    return _LIB.ozaki2_dgemm_noalloc(p, q, r, A, lda, B, ldb, C, ldc, s, mode, stream)
 
 
 def ozaki2_dgemm_ex(transa, transb, p, q, r, alpha, A, lda, B, ldb, beta, C, ldc, s, mode, stream) -> int:

@@ -189,6 +189,31 @@ struct State {
 
 State g;
 
+// Workspace of ozaki2_dgemm_noalloc: a fixed device array, one copy per GPU the library
+// runs on (it exists from the module's load on that GPU until the process ends).  In host
+// code `scratch` names a host-side stand-in, not device memory: its device address is
+// resolved once per device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) unsigned char scratch[OZ2_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};  // per device ordinal; filled on the first call there
+
+// The scratch array's device address on the current device (no allocation).
+int scratch_workspace(char** base) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return OZ2_ERR_HIP;
+  if (dev >= kMaxDevices) return OZ2_ERR_UNSUPPORTED;
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return OZ2_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *base = static_cast<char*>(g_scratch_ptr[dev]);
+  return OZ2_OK;
+}
+
 int acquire_workspace(size_t need, char** base) {
   if (g.user != nullptr) {
     if (g.user_bytes < need) return OZ2_ERR_WORKSPACE;
@@ -243,7 +268,9 @@ int copy_rows_2d(void* dst, size_t dpitch, const void* src, size_t spitch, size_
   return OZ2_OK;
 }
 
-int run(const Call& c, void* stream, const oz2_dump_t* dump) {
+// use_scratch: the workspace is the fixed scratch array (ozaki2_dgemm_noalloc), checked
+// against its size before any HIP call; otherwise the caller's or the library's buffer.
+int run(const Call& c, void* stream, const oz2_dump_t* dump, bool use_scratch = false) {
   int rc = validate(c, dump);
   if (rc != OZ2_OK) return rc;
   const int p = c.p, q = c.q, r = c.r, s = c.s, mode = c.mode;
@@ -252,7 +279,12 @@ int run(const Call& c, void* stream, const oz2_dump_t* dump) {
   const bool accu = mode == OZ2_ACCU;
   const Layout lay = make_layout(p, q, r, s);
   char* base = nullptr;
-  if ((rc = acquire_workspace(lay.total, &base)) != OZ2_OK) return rc;
+  if (use_scratch) {
+    if (lay.total > OZ2_NOALLOC_SCRATCH_BYTES) return OZ2_ERR_WORKSPACE;
+    if ((rc = scratch_workspace(&base)) != OZ2_OK) return rc;
+  } else if ((rc = acquire_workspace(lay.total, &base)) != OZ2_OK) {
+    return rc;
+  }
   Work w = bind(lay, base, p, q, r, s, accu);
   w.tau = tau_table(s);
   oz2_dump_t dz{};
@@ -324,6 +356,12 @@ int ozaki2_dgemm_ex(int transa, int transb, int p, int q, int r, double alpha, c
                     const double* B, int ldb, double beta, double* C, int ldc, int s, int mode, void* stream) {
   const Call c{transa, transb, p, q, r, alpha, A, lda, B, ldb, beta, C, ldc, s, mode};
   return run(c, stream, nullptr);
+}
+
+int ozaki2_dgemm_noalloc(int p, int q, int r, const double* A, int lda, const double* B, int ldb, double* C, int ldc,
+                         int s, int mode, void* stream) {
+  const Call c{OZ2_OP_N, OZ2_OP_N, p, q, r, 1.0, A, lda, B, ldb, 0.0, C, ldc, s, mode};
+  return run(c, stream, nullptr, true);
 }
 
 int ozaki2_dgemm_debug(int p, int q, int r, const double* A, int lda, const double* B, int ldb, double* C, int ldc,
@@ -445,7 +483,8 @@ const char* ozaki2_status_string(int status) {
     case OZ2_ERR_UNSUPPORTED:
       return "unsupported: q above OZ2_MAX_Q, a launch grid beyond its limits, or a P_t dump with q above OZ2_MAX_Q_P_DUMP";
     case OZ2_ERR_WORKSPACE:
-      return "workspace too small or device allocation failed";
+      return "workspace too small (a caller buffer, or the fixed scratch of ozaki2_dgemm_noalloc: "
+             "OZ2_NOALLOC_SCRATCH_BYTES) or device allocation failed";
     case OZ2_ERR_HIP:
       return "HIP runtime or kernel launch error";
     default:

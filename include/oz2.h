@@ -58,7 +58,8 @@ enum {
   OZ2_ERR_ARG = 1,         /* invalid size, leading dimension, pointer, s or mode */
   OZ2_ERR_UNSUPPORTED = 2, /* q > OZ2_MAX_Q, a size whose launch grid would not fit, or a raw P_t
                               dump requested with q > OZ2_MAX_Q_P_DUMP */
-  OZ2_ERR_WORKSPACE = 3,   /* caller workspace too small, or device allocation failed */
+  OZ2_ERR_WORKSPACE = 3,   /* caller workspace or the fixed scratch of ozaki2_dgemm_noalloc too small,
+                              or device allocation failed */
   OZ2_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 };
 
@@ -91,6 +92,27 @@ enum {
  */
 int ozaki2_dgemm(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
                  double* C, int ldc, int s, int mode, void* stream);
+
+/*
+ * ozaki2_dgemm_noalloc -- the product of ozaki2_dgemm (same arguments, kernels and result)
+ * for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library call) and ignores ozaki2_set_workspace: its workspace is a
+ * fixed device array of OZ2_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, which
+ * exists from the library's load on that GPU until the process ends.  The first call on a
+ * device resolves the array's address there (hipGetSymbolAddress, no allocation).
+ *   Size limit: a product whose ozaki2_workspace_size exceeds OZ2_NOALLOC_SCRATCH_BYTES is
+ *   rejected with OZ2_ERR_WORKSPACE before anything is launched (square products:
+ *   n = 2048 fits for every s, n = 3072 up to s = 9, n = 4096 up to s = 5).
+ *   Sharing: every call on one GPU uses that GPU's one array, so calls that may overlap on
+ *   one GPU (different streams, or host threads) race and must be ordered by the caller.
+ *   The kernels clear what must start at zero themselves; nothing carries over between
+ *   calls.
+ * Returns OZ2_OK, OZ2_ERR_ARG, OZ2_ERR_UNSUPPORTED, OZ2_ERR_WORKSPACE or OZ2_ERR_HIP.
+ */
+#define OZ2_NOALLOC_SCRATCH_BYTES (256ull << 20)
+int ozaki2_dgemm_noalloc(int p, int q, int r, const double* A, int lda, const double* B, int ldb,
+                         double* C, int ldc, int s, int mode, void* stream);
 
 /* Operation applied to an input matrix by ozaki2_dgemm_ex. */
 typedef enum {

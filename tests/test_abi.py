@@ -78,6 +78,27 @@ def test_argument_validation_before_launch(lib):
     assert run(p=0) == lib.OZ2_OK                     # empty: no work, nothing launched
     assert run(r=0) == lib.OZ2_OK
     assert lib.ozaki2_dgemm_debug(8, 8, 8, A, 8, B, 8, C, 8, 1, 0, None, None) == lib.OZ2_ERR_ARG
+
+
+def test_noalloc_checks_before_launch(lib):
+    """ozaki2_dgemm_noalloc validates like ozaki2_dgemm and rejects a product whose workspace
+    exceeds its fixed scratch, all before any HIP call (so this runs without a GPU)."""
+    A, B, C = 0x10000, 0x20000000, 0x40000000  # never dereferenced
+    call = lib.ozaki2_dgemm_noalloc
+    assert call(8, 8, 8, A, 8, B, 8, C, 8, 1, 0, None) == lib.OZ2_ERR_ARG
+    assert call(8, 8, 8, A, 8, B, 8, C, 8, 8, 2, None) == lib.OZ2_ERR_ARG
+    assert call(8, 8, 8, A, 8, B, 8, None, 8, 8, 0, None) == lib.OZ2_ERR_ARG
+    assert call(0, 8, 8, A, 8, B, 8, C, 8, 8, 0, None) == lib.OZ2_OK
+    big = (4096, 4096, 4096, 14)
+    assert lib.ozaki2_workspace_size(*big, 0) > lib.OZ2_NOALLOC_SCRATCH_BYTES
+    n, _, _, s = big
+    assert call(n, n, n, A, n, B, n, C, n, s, 0, None) == lib.OZ2_ERR_WORKSPACE
+    assert "ozaki2_dgemm_noalloc" in lib.ozaki2_status_string(lib.OZ2_ERR_WORKSPACE)
+    # square products at the largest s the scratch holds (documented in the header)
+    for n, s_max in ((2048, 20), (3072, 9), (4096, 5)):
+        assert lib.ozaki2_workspace_size(n, n, n, s_max, 1) <= lib.OZ2_NOALLOC_SCRATCH_BYTES
+        if s_max < 20:
+            assert lib.ozaki2_workspace_size(n, n, n, s_max + 1, 0) > lib.OZ2_NOALLOC_SCRATCH_BYTES
     # the raw P_t dump is exact int32 only without K-blocking
     dump = lib.OZ2Dump(P=0x60000000)
     q = lib.OZ2_MAX_Q_P_DUMP + 1
