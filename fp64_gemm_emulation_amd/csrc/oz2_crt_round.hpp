@@ -4,7 +4,7 @@
 //   crt_accumulate  acc[k] += R_t W_t[k]  (kW-bit limbs of the CRT weights, exact FMAs)
 //   crt_reduce      acc -= k M with k the nearest integer to sum_t R_t W_t / M
 //   crt_normalize   acc[0..L-2] -> [0, 2^kW), carries moved up
-//   crt_round       RN(X) 2^scale
+//   crt_round       RN(X 2^scale), rounded once (also below the normal range)
 //   crt_words       the 32-bit two's-complement words of X (validation)
 // The limb sums X = sum_k acc[k] 2^(kW k) stay exact integers below 2^53 in magnitude.
 //
@@ -69,11 +69,11 @@ __host__ __device__ inline void crt_normalize(double (&acc)[L]) {
   }
 }
 
-// RN(X) * 2^scale for normalised limbs (exact scaling unless the result is subnormal).
+// RN(X) to 53 bits for normalised limbs (X itself when |X| < 2^53).
 template <int L, int W, int kTopExp>
-__host__ __device__ inline double crt_round(const double (&a)[L], int scale) {
+__host__ __device__ inline double crt_round53(const double (&a)[L]) {
   if constexpr (L == 1) {
-    return ldexp(a[0], scale);  // |X| < 2^53: exact
+    return a[0];  // |X| < 2^53: exact
   } else {
     constexpr double kUp = pow2i(W), kUp2 = pow2i(2 * W);
     constexpr double kThr = pow2i(52 - W);
@@ -96,7 +96,7 @@ __host__ __device__ inline double crt_round(const double (&a)[L], int scale) {
       if (j > 2) zj *= pow2i(W * (j - 2));  // exact
       if (fabs(h[j]) >= kThr) z = zj;
     }
-    return ldexp(z, scale);
+    return z;
   }
 }
 
@@ -125,6 +125,52 @@ __host__ __device__ inline void crt_words(const double (&a)[L], uint32_t (&out)[
   }
 #pragma unroll
   for (int k = 0; k < 5; ++k) out[k] = static_cast<uint32_t>(x[k / 2] >> (32 * (k % 2)));
+}
+
+// RN(X 2^scale) for a result below the normal range, rounded once.  With g = -1074 - scale > 0
+// the result is the multiple of 2^-1074 nearest to X 2^scale (ties to an even multiple):
+// round(|X| / 2^g) 2^-1074 with the sign of X, taken from X's exact 160-bit two's-complement
+// form.  Only results below 2^-1022 come here (rare), where |X| < 2^(52 + g).
+template <int L, int W>
+__host__ __device__ inline double crt_round_subnormal(const double (&a)[L], int scale) {
+  uint32_t w[5];
+  crt_words<L, W>(a, w);
+  const bool neg = (w[4] >> 31) != 0;
+  uint64_t m[4] = {w[0] | (static_cast<uint64_t>(w[1]) << 32), w[2] | (static_cast<uint64_t>(w[3]) << 32), w[4], 0};
+  if (neg) {  // magnitude of the 160-bit two's-complement value
+    m[0] = ~m[0] + 1;
+    m[1] = ~m[1] + (m[0] == 0 ? 1 : 0);
+    m[2] = (~m[2] + (m[0] == 0 && m[1] == 0 ? 1 : 0)) & 0xFFFFFFFFull;
+  }
+  const int g = -1074 - scale;  // > 0: the bit position of the result's unit
+  uint64_t y = 0;
+  bool round_bit = false, sticky = false;
+  if (g <= 160) {  // |X| < 2^160: beyond that the result is below half a unit, hence 0
+    const int wi = g >> 6, bo = g & 63;  // y = |X| >> g (below 2^53)
+    y = (m[wi] >> bo) | (bo != 0 && wi < 3 ? m[wi + 1] << (64 - bo) : 0);
+    const int wr = (g - 1) >> 6, br = (g - 1) & 63;  // the bit below the unit, and all below it
+    round_bit = ((m[wr] >> br) & 1u) != 0;
+    sticky = (m[wr] & ((uint64_t{1} << br) - 1)) != 0;
+    for (int k = 0; k < wr; ++k) sticky = sticky || m[k] != 0;
+  }
+  if (round_bit && (sticky || (y & 1u) != 0)) ++y;
+  const double r = ldexp(static_cast<double>(y), -1074);  // exact: y <= 2^53
+  return neg ? -r : r;
+}
+
+// RN(X 2^scale) for normalised limbs, rounded once: X rounded to 53 bits and scaled exactly
+// when the result is normal; a result below 2^-1022 with scale < -1074 (where the
+// subnormal grid is coarser than X's integer grid) takes crt_round_subnormal.  With
+// scale >= -1074 a result below 2^-1022 has |X| < 2^52, so RN53(X) = X and ldexp is exact.
+template <int L, int W, int kTopExp>
+__host__ __device__ inline double crt_round(const double (&a)[L], int scale) {
+  const double z = crt_round53<L, W, kTopExp>(a);
+  if (scale < -1074 && z != 0.0) {
+    // z is an integer-valued double, |z| >= 1: its unbiased exponent is floor(log2 |z|)
+    const int ez = static_cast<int>((__builtin_bit_cast(uint64_t, z) >> 52) & 0x7FF) - 1023;
+    if (ez + scale < -1022) return crt_round_subnormal<L, W>(a, scale);
+  }
+  return ldexp(z, scale);
 }
 
 }  // namespace oz2

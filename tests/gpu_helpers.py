@@ -44,11 +44,10 @@ def assert_chat_close(c_gpu, c_ref, tol, what=""):
 
 
 def assert_correctly_rounded(c_gpu, c_ref, what=""):
-    """C is RN(X) 2^-(d_i + b_j) on the GPU and RN(X 2^-(d_i + b_j)) in the oracle: the same
-    double wherever the result is normal (below that, the scaling may round a second time)."""
-    normal = (np.abs(c_ref) >= 2.0 ** -1021) | (c_ref == 0)
-    bad = normal & (c_gpu != c_ref)
-    assert not bad.any(), f"{what}: {bad.sum()} normal entries differ from the correctly rounded value"
+    """C is RN(X 2^-(d_i + b_j)) rounded once on the GPU and in the oracle, below the normal
+    range too: the same double in every entry (signed zeros included)."""
+    bad = (c_gpu != c_ref) | (np.signbit(c_gpu) != np.signbit(c_ref))
+    assert not bad.any(), f"{what}: {bad.sum()} entries differ from the correctly rounded value"
 
 
 def compare_full(out, ref, A, B, s, mode):

@@ -108,6 +108,38 @@ def cases_for(s, rng):
     return sorted(xs)
 
 
+def rn_scaled(x, sc):
+    """RN(x 2^sc) rounded once: Python's int -> float conversion and int / int true division
+    are correctly rounded (to nearest, ties to even), below the normal range too."""
+    return float(x << sc) if sc >= 0 else x / (1 << -sc)
+
+
+def subnormal_cases(s, rng):
+    """(X, scale) pairs whose result X 2^scale lies below 2^-1022: X in every binade (with
+    random low bits, exact ties at the result's unit 2^g, and their neighbours), and scales
+    that put the result's unit at each bit position g from X's low end up past its top
+    (down to results that round to 0 or to the smallest subnormal)."""
+    M = math.prod(moduli(s))
+    T = tau(M)
+    out = []
+    for e in range(1, T + 1):
+        xs = [rng.randint(2 ** (e - 1), 2**e - 1)] if e > 1 else [1]
+        for x in xs:
+            n = x.bit_length()
+            for g in sorted({1, 2, max(1, n - 53), max(1, n - 52), max(1, n - 20), n - 1 if n > 1 else 1, n, n + 1, n + 2}):
+                sc = -1074 - g
+                tie = ((x >> g) << g) | (1 << (g - 1))                 # exactly halfway at unit 2^g
+                for v in (x, tie, tie - 1, tie + 1, tie + (1 << g)):
+                    if 0 < v <= 2**T and abs(v) * 2.0 ** -g < 2.0**52:
+                        out.extend([(v, sc), (-v, sc)])
+    # around the normal boundary: results just below and at 2^-1022
+    for g in (1, 3, 30):
+        for v in ((1 << (52 + g)) - 1, (1 << (52 + g)) - (1 << (g - 1)), (1 << (52 + g)) - (1 << g) - (1 << (g - 1))):
+            if v <= 2**T:
+                out.extend([(v, -1074 - g), (-v, -1074 - g)])
+    return out
+
+
 def scale_for(x, rng):
     """A scale that keeps |RN(x)| 2^scale normal and finite."""
     if x == 0:
@@ -125,7 +157,7 @@ def test_crt_arith_exact_words_and_rounding(harness, s):
         sc = scale_for(x, rng)
         lines.append(f"{s} {sc} " + " ".join(str(x % m) for m in ms))
         words = [(x >> (32 * k)) & 0xFFFFFFFF for k in range(5)]
-        val = math.ldexp(float(x), sc)                        # float(int) rounds to nearest even
+        val = rn_scaled(x, sc)
         bits = struct.unpack("<Q", struct.pack("<d", val))[0]
         want.append(" ".join(f"{w:08x}" for w in words) + f" {bits:016x}")
     res = subprocess.run([harness], input="\n".join(lines) + "\n", capture_output=True, text=True)
@@ -154,3 +186,26 @@ def test_crt_arith_cases_cover_ties_and_binades():
     missing = [(e, neg, a, b, c) for e in range(58, T) for neg in (False, True)
                for a in (0, 1) for b in (0, 1) for c in (False, True) if (e, neg, a, b, c) not in seen]
     assert not missing, missing[:5]
+
+
+@pytest.mark.parametrize("s", [2, 3, 8, 14, 18, 20])
+def test_crt_arith_subnormal_results_rounded_once(harness, s):
+    """Results below the normal range are RN(X 2^scale) itself, one rounding at the
+    subnormal unit 2^-1074 (ties to even), not X rounded to 53 bits and then again."""
+    rng = random.Random(2000 + s)
+    ms = moduli(s)
+    cases = subnormal_cases(s, rng)
+    lines, want = [], []
+    for x, sc in cases:
+        lines.append(f"{s} {sc} " + " ".join(str(x % m) for m in ms))
+        bits = struct.unpack("<Q", struct.pack("<d", rn_scaled(x, sc)))[0]
+        want.append(f"{bits:016x}")
+    res = subprocess.run([harness], input="\n".join(lines) + "\n", capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    got = [ln.split()[-1] for ln in res.stdout.split("\n")[: len(want)]]
+    bad = [(c, g, w) for c, g, w in zip(cases, got, want) if g != w]
+    assert not bad, f"s={s}: {len(bad)} of {len(cases)} differ, first: X, scale={bad[0][0]} got {bad[0][1]} want {bad[0][2]}"
+    # where X can exceed 53 bits, the cases reach results that a 53-bit rounding followed by a
+    # scaling gets wrong
+    twice = sum(1 for x, sc in cases if math.ldexp(float(x), sc) != rn_scaled(x, sc))
+    assert twice > 0 or tau(math.prod(ms)) < 54

@@ -105,6 +105,40 @@ def test_lines_whose_products_all_vanish(oz, mode):
     assert not c[17, :].any() and not c[:, 9].any()
 
 
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_subnormal_results_rounded_once(oz, mode):
+    """Entries of C below 2^-1022, s = 20: rows of A scaled by 2^-1000 against columns of B
+    scaled by 2^-60 (normal inputs, subnormal products), a row of subnormal entries of A,
+    and rows built so that (AB)_ij = 2^-1074 (Y + 1/2 -+ 2^-56) exactly, where rounding X to
+    53 bits and then scaling lands on the tie and rounds to the wrong neighbour.  Every entry
+    must be the correctly rounded RN(X 2^-(d_i + b_j)), one rounding at the subnormal unit."""
+    A = generate(60, 300, 1.0, 81)
+    B = generate(300, 40, 1.0, 82)
+    A[:20, :] = np.ldexp(A[:20, :], -1000)
+    B[:, :15] = np.ldexp(B[:, :15], -60)
+    A[25, :] = np.ldexp(A[25, :], -1060)            # subnormal inputs
+    B[:, 30:34] = 0.0
+    B[0:2, 30:34] = 2.0 ** -75
+    for k, (y, sgn) in enumerate([(5, -1), (4, 1), (1, -1), (2, 1), (1001, -1), (1000, 1)]):
+        for neg in (False, True):
+            i = 40 + 2 * k + neg
+            A[i, :] = 0.0
+            A[i, 0] = (2 * y + 1) * 2.0 ** -1000
+            A[i, 1] = sgn * 2.0 ** -1055
+            if neg:
+                A[i, :2] = -A[i, :2]
+    out, ref = _full_case(oz, A, B, 20, mode, "subnormal C")
+    c = ref["C"]
+    tiny = (c != 0) & (np.abs(c) < 2.0 ** -1022)
+    assert tiny.sum() > 500, "the case must produce subnormal results"
+    d, b = ref["d"], ref["b"]
+    twice = sum(1 for i, j in zip(*np.nonzero(tiny))
+                if np.ldexp(float(int(ref["X"][i, j])), -int(d[i] + b[j])) != c[i, j])
+    assert twice >= 48, "the built rows must reach results that two roundings get wrong"
+    assert np.array_equal(out["C"].cpu().numpy()[40:52, 30] / 2.0 ** -1074,
+                          [5, -5, 5, -5, 1, -1, 3, -3, 1001, -1001, 1001, -1001])
+
+
 def _block_spread(rows, q, seed):
     """rows x q with every 256-long block of a line at its own scale: exponent gaps to the
     line maximum of 0, 3, 7, 9 and about 1000, an all-zero block, a block of subnormals,
