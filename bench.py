@@ -4,9 +4,10 @@
 A step is one whole ozaki2_dgemm call (scaling, residues, s INT8 GEMMs, CRT) on the
 synthetic workload, inputs already resident in HBM.  The metric is effective FP64
 TFLOPS = 2 p q r / t ("Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs", Part I
-section 3).  Stage times come from HIP events the library records on the launch
-stream between its stages; the GEMM stage is one kernel launch (all s moduli), so its
-average event interval is that kernel's average launch duration.
+section 3), timed over plain calls.  The per-stage breakdown comes from a second loop of
+as many calls with the HIP events the library records on the launch stream between its
+stages; the GEMM stage is one kernel launch (all s moduli), so its average event interval
+is that kernel's average launch duration.
 
 Prints one JSON line.  Only one GPU is supported: --gpus above 1 exits with a message.
 """
@@ -72,21 +73,45 @@ def cpu_baseline(A, B, s, mode, rows, cols):
         blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas_threads = 1
-    rows, cols = min(rows, A.shape[0]), min(cols, B.shape[1])
+    p, q, r = A.shape[0], A.shape[1], B.shape[1]
+    rows, cols = min(rows, p), min(cols, r)
     stage_s = {}
     t0 = time.perf_counter()
     oracle.ozaki2_sample(A, B, s, mode, np.arange(rows), np.arange(cols), timings=stage_s)
     dt = time.perf_counter() - t0
-    flops = 2.0 * rows * A.shape[1] * cols
+    flops = 2.0 * rows * q * cols
+    # The whole product, extrapolated stage by stage from the sample by the ratio of each
+    # stage's work: the fast scalings and the residues grow with the lines they cover (rows
+    # of A plus columns of B), the products and the CRT with the outputs.  The accu scaling
+    # of the sample already quantizes the whole operands and forms the bound product for the
+    # sampled rows and columns (rows r + p cols entries); its factor is that product's ratio,
+    # an upper bound since the quantization does not grow.
+    line_ratio = (p + r) / (rows + cols)
+    out_ratio = (p * r) / (rows * cols)
+    bound_ratio = (p * r) / (rows * r + p * cols)
+    factors = {"scaling": bound_ratio if mode == "accu" else line_ratio, "residues": line_ratio,
+               "gemm": out_ratio, "crt": out_ratio}
+    full = {k: stage_s[k] * factors[k] for k in factors}
+    full_s = sum(full.values())
     return {
         "value": flops / dt / 1e12,
         "unit": "effective FP64 TFLOPS",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"C[0:{rows}, 0:{cols}] of the {A.shape[0]}x{A.shape[1]}x{B.shape[1]} workload "
+        "sample": f"C[0:{rows}, 0:{cols}] of the {p}x{q}x{r} workload "
                   f"(scalings of the sampled rows/columns, their residues, s products, CRT, inverse scaling)",
         "seconds": dt,
         "stage_seconds": stage_s,
+        "full_product_extrapolated": {
+            "seconds": full_s,
+            "effective_tflops": 2.0 * p * q * r / full_s / 1e12,
+            "stage_seconds": full,
+            "stage_factors": factors,
+            "sample_fraction_of_outputs": rows * cols / (p * r),
+            "basis": "each stage's sample time times its work ratio: lines (p + r) / (rows + cols) "
+                     "for fast scaling and residues, outputs p r / (rows cols) for products and CRT, "
+                     "bound-product entries p r / (rows r + p cols) for accu scaling (an upper bound)",
+        },
         "host_cpus": len(os.sched_getaffinity(0)),
         "cpu_model": cpu_model(),
     }
@@ -157,6 +182,47 @@ def mfma_ceiling(blocks=1024, rounds=3584, reps=5):
     return ops / (ms * 1e-3) / 1e12
 
 
+def gemm_vs_shape_ceiling(call, s, n, rounds=3, calls=5):
+    """The GEMM stage against the register-only MFMA kernel of the GEMM's exact shape
+    (libozcalib.so: the GEMM's grid of 256 x 256 tiles over all planes, 8 waves of 8 x 4
+    blocks, fragments changing every 64-deep stage, one workgroup per CU), alternated in
+    rounds so that both run at the same thermal state.  Both do s 2 n^3 int8 operations per
+    launch; what separates them is the GEMM's memory traffic and epilogue."""
+    import ctypes
+    import torch
+    from fp64_gemm_emulation_amd import binding
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp64_gemm_emulation_amd", "libozcalib.so"))
+    lib.oz2calib_mfma_i8_gemm_shape.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                ctypes.c_void_p]
+    lib.oz2calib_mfma_i8_gemm_shape.restype = ctypes.c_int
+    tiles, stages = (n // 256) ** 2 * s, n // 64
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (1024 * 12 * 512 * 4,), dtype=torch.int32, device="cuda",
+                        generator=gen)
+    out = torch.empty(tiles * 512, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    ops = s * 2.0 * n ** 3
+    gemm_ms, ceil_ms = [], []
+    for _ in range(rounds):
+        assert binding.ozaki2_timing_begin(calls) == binding.OZ2_OK
+        for _ in range(calls):
+            call(stream)
+        rc, st, k = binding.ozaki2_timing_end()
+        assert rc == binding.OZ2_OK and k == calls
+        gemm_ms.append(st[2] / calls)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            assert lib.oz2calib_mfma_i8_gemm_shape(src.data_ptr(), tiles, stages, out.data_ptr(), stream.cuda_stream) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ceil_ms.append(e0.elapsed_time(e1) / calls)
+    g, c = sum(gemm_ms) / rounds, sum(ceil_ms) / rounds
+    return {"gemm_ms": g, "gemm_shape_ceiling_ms": c, "gemm_tops": ops / (g * 1e-3) / 1e12,
+            "gemm_shape_ceiling_tops": ops / (c * 1e-3) / 1e12, "gemm_over_gemm_shape_ceiling": c / g,
+            "rounds": rounds, "launches_per_round": calls}
+
+
 def exact_dot_samples(A, B, rows, cols):
     """Exact (A B)_ij for the sampled entries, as Fractions (integer arithmetic on the FP64
     significands; independent of the library and of the test oracle)."""
@@ -200,7 +266,7 @@ def sweep(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream(device=dev)
     rng = np.random.default_rng(99)
     for n in args.sweep_n:
         A = generate(n, n, args.sweep_phi, 1)
@@ -246,6 +312,82 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+def overlap_probe(args):
+    """Upper bound on what overlapping one product's stages with another's can gain: the
+    same K products (n x n fast, the generator of the n = 2048 workload) run back to back on
+    one stream, then split over two streams of default priority with a workspace each, so
+    the scheduler may run any stage of one product beside any stage of the other (the
+    preprocessing of the next beside the GEMMs of the current, as in an overlap by modulus
+    group, is one such schedule), and one call captured in a HIP graph and replayed (the
+    GPU time of a call without the host's launch work).  One JSON line per size."""
+    import numpy as np
+    import torch
+
+    from fp64_gemm_emulation_amd import binding
+    from fp64_gemm_emulation_amd.workloads import generate
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for n in args.overlap_probe:
+        s = args.probe_s
+        A = generate(n, n, 0.5, 1)
+        B = generate(n, n, 0.5, 2)
+        Ad = binding.colmajor(torch.from_numpy(np.ascontiguousarray(A)).to(dev))
+        Bd = binding.colmajor(torch.from_numpy(np.ascontiguousarray(B)).to(dev))
+        need = binding.ozaki2_workspace_size(n, n, n, s, binding.OZ2_FAST)
+        ws = [torch.empty(need + 256, dtype=torch.uint8, device=dev) for _ in range(2)]
+        base = [(w.data_ptr() + 255) // 256 * 256 for w in ws]
+        outs = [binding.empty_colmajor(n, n, device=dev) for _ in range(2)]
+        streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+        K = args.probe_calls
+
+        def run(two):
+            for k in range(K):
+                j = k % 2 if two else 0
+                binding.ozaki2_set_workspace(base[j], need)
+                binding.dgemm(Ad, Bd, s, "fast", out=outs[j], stream=streams[j])
+
+        results = {}
+        for label, two in (("one_stream", False), ("two_streams", True), ("one_stream_again", False)):
+            run(two)                      # warm-up of this arrangement
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run(two)
+            torch.cuda.synchronize()
+            results[label] = (time.perf_counter() - t0) * 1e3 / K
+        assert torch.equal(outs[0], outs[1])
+        # one call captured in a HIP graph and replayed on one stream: the same kernels with
+        # the host's per-call launch work taken out, i.e. the GPU time of a call
+        binding.ozaki2_set_workspace(base[0], need)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=streams[0]):
+            binding.dgemm(Ad, Bd, s, "fast", out=outs[0], stream=streams[0])
+        outs[0].fill_(float("nan"))
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        results["one_stream_graph_replay"] = (time.perf_counter() - t0) * 1e3 / K
+        assert torch.equal(outs[0], outs[1])
+        del graph
+        torch.cuda.synchronize()
+        binding.ozaki2_set_workspace(None, 0)
+        serial = 0.5 * (results["one_stream"] + results["one_stream_again"])
+        print(json.dumps({"overlap_probe": "two independent products on two streams vs one stream",
+                          "n": n, "s": s, "mode": "fast", "calls": K,
+                          "ms_per_call": results, "two_streams_over_one_stream": results["two_streams"] / serial,
+                          "eff_tflops_one_stream": 2.0 * n ** 3 / (serial * 1e-3) / 1e12,
+                          "eff_tflops_two_streams": 2.0 * n ** 3 / (results["two_streams"] * 1e-3) / 1e12,
+                          "eff_tflops_graph_replay": 2.0 * n ** 3 / (results["one_stream_graph_replay"] * 1e-3) / 1e12}),
+              flush=True)
+        del Ad, Bd, ws, outs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,7 +397,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context figures (native FP64 matmul, MFMA ceiling on random operands)")
-    ap.add_argument("--cpu-rows", type=int, default=192)
+    ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--cpu-cols", type=int, default=2048)
     ap.add_argument("--zero-inputs", action="store_true",
                     help="diagnostic: A = B = 0 (every residue plane is zero), to show the data-dependent "
@@ -269,6 +411,11 @@ def main():
     ap.add_argument("--sweep-modes", nargs="+", default=["fast", "accu"])
     ap.add_argument("--sweep-phi", type=float, default=0.5)
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--overlap-probe", type=int, nargs="+", default=None, metavar="N",
+                    help="two streams against one for independent n x n fast products (sizes N), instead "
+                         "of the benchmark line")
+    ap.add_argument("--probe-s", type=int, default=14)
+    ap.add_argument("--probe-calls", type=int, default=60)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -278,6 +425,9 @@ def main():
 
     if args.sweep:
         sweep(args)
+        return
+    if args.overlap_probe:
+        overlap_probe(args)
         return
 
     import numpy as np
@@ -298,7 +448,10 @@ def main():
     Ad = binding.colmajor(torch.from_numpy(np.ascontiguousarray(A)).to(dev))
     Bd = binding.colmajor(torch.from_numpy(np.ascontiguousarray(B)).to(dev))
     C = binding.empty_colmajor(n, n, device=dev)
-    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    # a stream of our own (default priority): launches on the legacy null stream wait on
+    # implicit synchronisation and leave the GPU idle between kernels
+    stream = torch.cuda.Stream(device=dev)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 27, dtype=torch.float64, device=dev).fill_(1.0)   # 1 GiB
@@ -311,20 +464,29 @@ def main():
         binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
     torch.cuda.synchronize()
 
-    assert binding.ozaki2_timing_begin(args.steps) == binding.OZ2_OK
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # The timed steps: plain calls, as a user makes them (no timing events between the
+    # stages: each event record leaves the GPU idle for a few microseconds).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for k in range(args.steps):
+        binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc, flags = binding.ozaki2_get_flags()
+
+    # Then the same number of calls again with the library's stage events (HIP events on the
+    # launch stream between the stages) for the per-stage breakdown and the GEMM kernel's
+    # average duration, and one event per call for the per-call spread.
+    assert binding.ozaki2_timing_begin(args.steps) == binding.OZ2_OK
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     marks[0].record(stream)
     for k in range(args.steps):
         binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
         marks[k + 1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
     rc, stage_ms, ncalls = binding.ozaki2_timing_end()
     assert rc == binding.OZ2_OK and ncalls == args.steps
-    rc, flags = binding.ozaki2_get_flags()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     eff_tflops = 2.0 * n ** 3 / (ms_per_step * 1e-3) / 1e12
@@ -348,9 +510,10 @@ def main():
         "gemm_frac_int8_peak": gemm_tops / PEAK_INT8_TOPS,
         "residues_per_s": 2.0 * s * n * n / (st[1] * 1e-3),
         "int8_macs_per_s": s * float(n) ** 3 / (st[2] * 1e-3),
-        "step_ms_median": per_step[len(per_step) // 2],
-        "step_ms_min": per_step[0],
-        "step_ms_max": per_step[-1],
+        # per call in the stage-timed loop (includes the stage events' idle gaps)
+        "step_ms_median_with_stage_events": per_step[len(per_step) // 2],
+        "step_ms_min_with_stage_events": per_step[0],
+        "step_ms_max_with_stage_events": per_step[-1],
     }
     result = {
         "metric": "effective FP64 TFLOPS (2n^3/t), n=8192 fast-14; per-stage ms breakdown",
@@ -386,6 +549,9 @@ def main():
         ceil_tops = mfma_ceiling()
         ctx["mfma_i8_ceiling_random_operands_tops"] = ceil_tops
         ctx["gemm_frac_of_mfma_ceiling"] = gemm_tops / ceil_tops
+        if n % 256 == 0 and n >= 2048:
+            ctx["gemm_vs_gemm_shape_ceiling_interleaved"] = gemm_vs_shape_ceiling(
+                lambda st: binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=st), s, n)
         result["context"] = ctx
     if not args.no_cpu_baseline and not args.zero_inputs:
         result["cpu_baseline"] = cpu_baseline(A, B, s, w.mode, args.cpu_rows, args.cpu_cols)

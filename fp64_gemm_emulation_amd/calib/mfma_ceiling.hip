@@ -44,6 +44,45 @@ __global__ __launch_bounds__(512, 1) void mfma_i8_ceiling_kernel(const v4i* __re
   out[blockIdx.x * 512 + tid] = x;
 }
 
+// The same instruction in the exact shape of the large-grid mod GEMM: one workgroup of 8
+// waves per 256 x 256 output tile (the GEMM's grid), each wave 8 x 4 blocks of 16 x 16 (32
+// accumulators) issued in the GEMM's order, and 12 fragments (8 of A, 4 of B) that all change
+// after every 32 MFMAs, as the GEMM reads new fragments for every 64-deep stage.  128 KiB of
+// LDS is held (never touched) so that one workgroup runs per CU, as for the GEMM.  What it
+// leaves out is the GEMM's memory traffic (copies into LDS, fragment reads) and its
+// epilogue, so the GEMM's rate over this one's is the cost of those at equal MFMA work.
+__global__ __launch_bounds__(512, 1) void mfma_i8_gemm_shape_kernel(const v4i* __restrict__ src, int stages,
+                                                                      int* __restrict__ out) {
+  __shared__ int lds_hold[128 * 1024 / 4];
+  const int tid = threadIdx.x;
+  v4i f[12];
+#pragma unroll
+  for (int g = 0; g < 12; ++g) f[g] = src[((blockIdx.x & 1023) * 12 + g) * 512 + tid];
+  v4i acc[8][4];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = v4i{};
+  for (int kt = 0; kt < stages; ++kt) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[mb], f[8 + nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 12; ++g) f[g] = rotate_bytes(f[g]);
+  }
+  int x = 0;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) x ^= acc[mb][nb][v];
+  if (x == 0x7fffffff) lds_hold[tid] = x;  // keeps the LDS allocation; practically never taken
+  out[blockIdx.x * 512 + tid] = x;
+}
+
 // src: blocks * 8 * 512 16-byte random words (device); out: blocks * 512 ints (device).
 // One round is 16 MFMAs of 16 x 16 x 64 per wave, 8 waves: 8 * 16 * 16384 = 2^21
 // multiply-adds per block.
@@ -51,5 +90,15 @@ extern "C" int oz2calib_mfma_i8(const void* src, int blocks, int rounds, int* ou
   if (!src || !out || blocks <= 0 || rounds <= 0) return 1;
   hipLaunchKernelGGL(mfma_i8_ceiling_kernel, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream),
                      static_cast<const v4i*>(src), rounds, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// src: 1024 * 12 * 512 16-byte random words (device); out: tiles * 512 ints (device).  One
+// workgroup per tile, each 8 waves x 32 MFMAs of 16 x 16 x 64 per stage: stages * 2^22
+// multiply-adds per tile.
+extern "C" int oz2calib_mfma_i8_gemm_shape(const void* src, int tiles, int stages, int* out, void* stream) {
+  if (!src || !out || tiles <= 0 || stages <= 0) return 1;
+  hipLaunchKernelGGL(mfma_i8_gemm_shape_kernel, dim3(tiles), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const v4i*>(src), stages, out);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
