@@ -297,7 +297,6 @@ int run(const Call& c, void* stream, const oz2_dump_t* dump, bool use_scratch = 
 
   Recorder rec(st);
   OZ2_TRY(rec.mark(0));
-  OZ2_TRY(oz2::launch_fill_u32(w.flags, 0u, 1, st));
   // rows of op(A) are contiguous when A is transposed; columns of op(B) unless B is
   const oz2::Operand opa{c.A, c.lda, c.transa == OZ2_OP_T};
   const oz2::Operand opb{c.B, c.ldb, c.transb == OZ2_OP_N};

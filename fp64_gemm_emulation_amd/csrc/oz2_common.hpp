@@ -106,11 +106,12 @@ struct ChunkOwner {
 // q_pad / 64).  Lane l of wave w owns row 16 w + l / 4 and physical chunk l % 4 of that
 // row's stage segment: a store instruction writes 1 KiB contiguous (16 rows x 64 bytes),
 // and a load instruction for one k reads 4 columns x 16 consecutive rows.
-__device__ __forceinline__ ChunkOwner owner_rows_of_a() {
+// (bx, by): the workgroup's coordinates in that grid.
+__device__ __forceinline__ ChunkOwner owner_rows_of_a(int bx, int by) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int stage = blockIdx.y;
-  const int row = blockIdx.x * 64 + wave * 16 + (lane >> 2);
+  const int stage = by;
+  const int row = bx * 64 + wave * 16 + (lane >> 2);
   return ChunkOwner{row, stage >> 2, 4 * (stage & 3) + ((lane & 3) ^ operand_swizzle(row & 15))};
 }
 
@@ -118,10 +119,11 @@ __device__ __forceinline__ ChunkOwner owner_rows_of_a() {
 // q_pad / 256).  Lane l of wave w owns column 4 w + l / 16 and slot l % 16: a load
 // instruction for one k reads 4 runs of 128 contiguous bytes, a store instruction writes
 // 4 runs of 256 contiguous bytes (4 rows x 64 bytes in each of the 4 stage tiles).
-__device__ __forceinline__ ChunkOwner owner_cols_of_b() {
+// (bx, by): the workgroup's coordinates in that grid.
+__device__ __forceinline__ ChunkOwner owner_cols_of_b(int bx, int by) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  return ChunkOwner{static_cast<int>(blockIdx.x) * 16 + wave * 4 + (lane >> 4), static_cast<int>(blockIdx.y), lane & 15};
+  return ChunkOwner{bx * 16 + wave * 4 + (lane >> 4), by, lane & 15};
 }
 
 // Byte offset of inner-dimension element l of row `row` (the inverse map, for validation).

@@ -47,7 +47,6 @@ template <bool MAXONLY>
 __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double* __restrict__ A, long lda, int p,
                                                                    int q, int nch, int* __restrict__ part_e,
                                                                    double* __restrict__ part_s,
-                                                                   unsigned* __restrict__ flags,
                                                                    int8_t* __restrict__ qout, int q_pad) {
   __shared__ int sh_e[kStatsRowGroups][kStatsColGroups][kWave];
   __shared__ double sh_s[kStatsRowGroups][kStatsColGroups][kWave];
@@ -63,18 +62,14 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
 
   double v[kStatsCols];
   int emax = kNoExp;
-  bool bad = false;
 #pragma unroll
   for (int k = 0; k < kStatsCols; ++k) {
     double x = 0.0;
     if (row_ok && l0 + k < q) x = base[static_cast<long>(k) * lda];
-    const bool nf = is_nonfinite(x);
-    bad |= nf;
-    x = nf ? 0.0 : x;
+    x = is_nonfinite(x) ? 0.0 : x;  // (flagged by the residue stage)
     v[k] = x;
     emax = max(emax, exponent_of(x));
   }
-  if (bad) atomicOr(flags, kFlagNonFinite);
   sh_e[g][w][lane] = emax;
   __syncthreads();
   int ec = kNoExp;
@@ -142,7 +137,6 @@ template <bool MAXONLY, int CB>
 __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                          int nch, int* __restrict__ part_e,
                                                          double* __restrict__ part_s,
-                                                         unsigned* __restrict__ flags,
                                                          int8_t* __restrict__ qout, int q_pad) {
   // grid: x = column j, y = groups of 4 CB blocks; one wave per (j, CB blocks)
   const int lane = threadIdx.x & 63;
@@ -152,18 +146,14 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
   const bool col_ok = j < r;  // columns up to the padded count when the bound input is written
   const double* col = B + static_cast<long>(col_ok ? j : 0) * ldb;
   double v[CB][4];
-  bool bad = false;
 #pragma unroll
   for (int b = 0; b < CB; ++b)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int l = (c0 + b) * kChunk + lane + kWave * k;
-      double x = (col_ok && c0 + b < nch && l < q) ? col[l] : 0.0;
-      const bool nf = is_nonfinite(x);
-      bad |= nf;
-      v[b][k] = nf ? 0.0 : x;
+      const double x = (col_ok && c0 + b < nch && l < q) ? col[l] : 0.0;
+      v[b][k] = is_nonfinite(x) ? 0.0 : x;  // (flagged by the residue stage)
     }
-  if (bad) atomicOr(flags, kFlagNonFinite);
 #pragma unroll
   for (int b = 0; b < CB; ++b) {
     const int c = c0 + b;
@@ -225,9 +215,13 @@ __global__ __launch_bounds__(256) void fast_exponents_kernel(int na, int nb, int
                                                              const double* __restrict__ ps_a,
                                                              const int* __restrict__ pe_b,
                                                              const double* __restrict__ ps_b, int* __restrict__ d,
-                                                             int* __restrict__ b, int tau) {
+                                                             int* __restrict__ b, int tau,
+                                                             unsigned* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the call's non-finite flag starts here: the residue stage, which runs after this
+  // kernel, sets it (no earlier kernel of the call touches it)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   if (idx >= na + nb) return;  // whole wave
   const bool is_a = idx < na;
   const int line = is_a ? idx : idx - na;
@@ -264,9 +258,11 @@ __global__ __launch_bounds__(256) void fast_exponents_kernel(int na, int nb, int
 }
 
 // accu: line max-abs exponents from block maxima.
+// Also starts the bound product's row / column maxima at 0 (the bound GEMM, which runs after
+// this kernel, accumulates them with atomics).
 __global__ void max_exponents_kernel(int na, int nb, int nch, const int* __restrict__ pe_a,
                                      const int* __restrict__ pe_b, int* __restrict__ e_row,
-                                     int* __restrict__ f_col) {
+                                     int* __restrict__ f_col, int* __restrict__ rho, int* __restrict__ gamma) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= na + nb) return;
   const bool is_a = idx < na;
@@ -274,10 +270,13 @@ __global__ void max_exponents_kernel(int na, int nb, int nch, const int* __restr
   const int* pe = (is_a ? pe_a : pe_b) + static_cast<long>(line) * nch;
   int e = kNoExp;
   for (int c = 0; c < nch; ++c) e = max(e, pe[c]);
-  if (is_a)
+  if (is_a) {
     e_row[line] = e;
-  else
+    rho[line] = 0;
+  } else {
     f_col[line] = e;
+    gamma[line] = 0;
+  }
 }
 
 // accu bound inputs of lines that are rows of a column-major matrix:
@@ -314,8 +313,10 @@ __global__ __launch_bounds__(256) void requant_kernel(int8_t* __restrict__ plane
 __global__ void accu_exponents_kernel(int na, int nb, const int* __restrict__ e_row,
                                       const int* __restrict__ f_col, const int* __restrict__ rho,
                                       const int* __restrict__ gamma, int* __restrict__ d,
-                                      int* __restrict__ b, int tau) {
+                                      int* __restrict__ b, int tau, unsigned* __restrict__ flags) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  // the call's non-finite flag starts here (set by the residue stage, which runs after)
+  if (idx == 0) *flags = 0u;
   if (idx >= na + nb) return;
   const bool is_a = idx < na;
   const int line = is_a ? idx : idx - na;
@@ -351,23 +352,23 @@ template <bool MAXONLY>
 // With qout (accu), the block-quantized bound input of every line up to nlines_pad is written
 // too (zeros past nlines), in the operand tile layout of q_pad columns.
 static void stats_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, int nch, int* pe, double* ps,
-                        unsigned* flags, int8_t* qout, hipStream_t st) {
+                        int8_t* qout, hipStream_t st) {
   if (nch == 0 || nlines == 0) return;
   const int ngrid = qout != nullptr ? nlines_pad : nlines;
   if (o.contig) {
     if (nch <= 32) {
       dim3 grid(ngrid, blocks_for(nch, 4 * 2));
       hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 2>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps,
-                         flags, qout, q_pad);
+                         qout, q_pad);
     } else {
       dim3 grid(ngrid, blocks_for(nch, 4 * 8));
       hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 8>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps,
-                         flags, qout, q_pad);
+                         qout, q_pad);
     }
   } else {
     dim3 grid(blocks_for(ngrid, kWave * kStatsRowGroups), nch);
     hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(kStatsThreads), 0, st, o.ptr, o.ld, nlines, q, nch, pe,
-                       ps, flags, qout, q_pad);
+                       ps, qout, q_pad);
   }
 }
 
@@ -375,8 +376,8 @@ template <bool MAXONLY>
 static hipError_t launch_stats(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
   int8_t* const qa = MAXONLY ? w.abar : nullptr;
   int8_t* const qb = MAXONLY ? w.bbar : nullptr;
-  stats_lines<MAXONLY>(a, w.p, w.p_pad, w.q, w.q_pad, w.nch, w.part_e_a, w.part_s_a, w.flags, qa, st);
-  stats_lines<MAXONLY>(b, w.r, w.r_pad, w.q, w.q_pad, w.nch, w.part_e_b, w.part_s_b, w.flags, qb, st);
+  stats_lines<MAXONLY>(a, w.p, w.p_pad, w.q, w.q_pad, w.nch, w.part_e_a, w.part_s_a, qa, st);
+  stats_lines<MAXONLY>(b, w.r, w.r_pad, w.q, w.q_pad, w.nch, w.part_e_b, w.part_s_b, qb, st);
   return hipGetLastError();
 }
 
@@ -392,7 +393,7 @@ hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w
   if (e != hipSuccess) return e;
   const int n = w.p + w.r;
   hipLaunchKernelGGL(fast_exponents_kernel, dim3(blocks_for(n, 4)), dim3(256), 0, st, w.p, w.r, w.nch,
-                     w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b, w.d, w.b, w.tau);
+                     w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b, w.d, w.b, w.tau, w.flags);
   return hipGetLastError();
 }
 
@@ -401,19 +402,16 @@ hipError_t launch_accu_bound_inputs(const Operand& a, const Operand& b, const Wo
   if (e != hipSuccess) return e;
   const int n = w.p + w.r;
   hipLaunchKernelGGL(max_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.nch,
-                     w.part_e_a, w.part_e_b, w.e_row, w.f_col);
+                     w.part_e_a, w.part_e_b, w.e_row, w.f_col, w.rho, w.gamma);
   requant_lines(w.abar, w.p, w.nch, w.q_pad, w.e_row, w.part_e_a, st);
   requant_lines(w.bbar, w.r, w.nch, w.q_pad, w.f_col, w.part_e_b, st);
-  // the bound GEMM accumulates maxima with atomics: start from 0
-  if ((e = launch_fill_i32(w.rho, 0, w.p, st)) != hipSuccess) return e;
-  if ((e = launch_fill_i32(w.gamma, 0, w.r, st)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
 hipError_t launch_accu_exponents(const Work& w, hipStream_t st) {
   const int n = w.p + w.r;
   hipLaunchKernelGGL(accu_exponents_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, w.p, w.r, w.e_row,
-                     w.f_col, w.rho, w.gamma, w.d, w.b, w.tau);
+                     w.f_col, w.rho, w.gamma, w.d, w.b, w.tau, w.flags);
   return hipGetLastError();
 }
 

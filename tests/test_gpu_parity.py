@@ -190,15 +190,29 @@ def test_inner_dimension_zero_gives_zero(oz):
     assert not C.cpu().numpy().any()
 
 
-def test_nonfinite_flagged(oz):
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_nonfinite_flagged(oz, mode):
+    """A non-finite input sets the flag of that call and only that call: untransposed operands
+    (one residue launch for both), a transposed A and a NaN in B (one launch each)."""
     import torch
     A = generate(40, 64, 0.5, 1)
     B = generate(64, 30, 0.5, 2)
     A[3, 4] = np.inf
-    oz.dgemm(to_device(A), to_device(B), 8, "fast")
+    oz.dgemm(to_device(A), to_device(B), 8, mode)
     rc, flags = oz.ozaki2_get_flags()
     assert rc == oz.OZ2_OK and flags & 1
-    oz.dgemm(to_device(generate(40, 64, 0.5, 1)), to_device(B), 8, "fast")
+    oz.dgemm(to_device(generate(40, 64, 0.5, 1)), to_device(B), 8, mode)
+    rc, flags = oz.ozaki2_get_flags()
+    assert rc == oz.OZ2_OK and flags == 0
+    oz.dgemm_ex(to_device(A.T.copy()), to_device(B), transa=True, s=8, mode=mode)
+    rc, flags = oz.ozaki2_get_flags()
+    assert rc == oz.OZ2_OK and flags & 1
+    B2 = B.copy()
+    B2[10, 7] = np.nan
+    oz.dgemm(to_device(generate(40, 64, 0.5, 1)), to_device(B2), 8, mode)
+    rc, flags = oz.ozaki2_get_flags()
+    assert rc == oz.OZ2_OK and flags & 1
+    oz.dgemm_ex(to_device(generate(40, 64, 0.5, 1).T.copy()), to_device(B), transa=True, s=8, mode=mode)
     rc, flags = oz.ozaki2_get_flags()
     assert rc == oz.OZ2_OK and flags == 0
     torch.cuda.synchronize()
