@@ -388,6 +388,74 @@ def overlap_probe(args):
         torch.cuda.empty_cache()
 
 
+def tile_probe(args):
+    """Lower bound on a GEMM fused with the CRT: a mod GEMM in the library's form with
+    256 x 256 and with 128 x 128 output tiles (libozcalib.so), alternated on the same random
+    int8 planes of the n x n, s-modulus product, beside the real product's GEMM and CRT
+    stages.  A fused kernel has to hold every output's s residues on chip, which rules out
+    the 256 x 256 tile; if the 128 x 128 GEMM alone already takes longer than the product's
+    GEMM stage plus its separate CRT, the fused kernel cannot win."""
+    import ctypes
+    import numpy as np
+    import torch
+
+    from fp64_gemm_emulation_amd import binding
+    from fp64_gemm_emulation_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    n, s = w.n, w.s
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp64_gemm_emulation_amd", "libozcalib.so"))
+    lib.oz2calib_gemm_tiles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.oz2calib_gemm_tiles.restype = ctypes.c_int
+    stream = torch.cuda.Stream(device=dev)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    planes = [torch.randint(-128, 128, (s * n * n,), dtype=torch.int8, device=dev, generator=gen) for _ in range(2)]
+    res = torch.empty(s * n * n, dtype=torch.uint8, device=dev)
+    ops = s * 2.0 * n ** 3
+
+    def tiles_ms(tile, calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            assert lib.oz2calib_gemm_tiles(planes[0].data_ptr(), planes[1].data_ptr(), n, s, tile, res.data_ptr(),
+                                           stream.cuda_stream) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls
+
+    A, B = w.inputs()
+    Ad = binding.colmajor(torch.from_numpy(np.ascontiguousarray(A)).to(dev))
+    Bd = binding.colmajor(torch.from_numpy(np.ascontiguousarray(B)).to(dev))
+    C = binding.empty_colmajor(n, n, device=dev)
+    for _ in range(2):
+        binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
+    tiles_ms(256, 1)
+    tiles_ms(128, 1)
+    t256, t128, stages = [], [], []
+    for _ in range(3):
+        t256.append(tiles_ms(256, 3))
+        t128.append(tiles_ms(128, 3))
+        assert binding.ozaki2_timing_begin(3) == binding.OZ2_OK
+        for _ in range(3):
+            binding.dgemm(Ad, Bd, s, w.mode, out=C, stream=stream)
+        rc, st, k = binding.ozaki2_timing_end()
+        assert rc == binding.OZ2_OK and k == 3
+        stages.append([v / k for v in st])
+    g256, g128 = sum(t256) / 3, sum(t128) / 3
+    gemm_ms = sum(x[2] for x in stages) / 3
+    crt_ms = sum(x[3] for x in stages) / 3
+    print(json.dumps({"tile_probe": "mod GEMM with 256 x 256 vs 128 x 128 output tiles (random int8 planes), and "
+                                    "the product's own GEMM and CRT stages, alternated",
+                      "workload": w.name, "n": n, "s": s,
+                      "gemm_tile256_ms": g256, "gemm_tile128_ms": g128,
+                      "tile256_tops": ops / (g256 * 1e-3) / 1e12, "tile128_tops": ops / (g128 * 1e-3) / 1e12,
+                      "product_gemm_stage_ms": gemm_ms, "product_crt_stage_ms": crt_ms,
+                      "tile128_over_product_gemm_plus_crt": g128 / (gemm_ms + crt_ms)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -415,6 +483,9 @@ def main():
                     help="two streams against one for independent n x n fast products (sizes N), instead "
                          "of the benchmark line")
     ap.add_argument("--probe-s", type=int, default=14)
+    ap.add_argument("--tile-probe", action="store_true",
+                    help="the mod GEMM with 256 x 256 against 128 x 128 tiles and the CRT stage (the bound on a "
+                         "GEMM fused with the CRT), instead of the benchmark line")
     ap.add_argument("--probe-calls", type=int, default=60)
     args = ap.parse_args()
 
@@ -428,6 +499,9 @@ def main():
         return
     if args.overlap_probe:
         overlap_probe(args)
+        return
+    if args.tile_probe:
+        tile_probe(args)
         return
 
     import numpy as np

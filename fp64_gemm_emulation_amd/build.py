@@ -2,8 +2,7 @@
 
 Each ``csrc/*.hip`` file is compiled to an object with hipcc in parallel, then the
 objects are linked into ``fp64_gemm_emulation_amd/liboz2.so`` (the library).  The
-measurement aid ``calib/mfma_ceiling.hip`` becomes ``libozcalib.so``, loaded only by
-bench.py.  Packed FP32 instructions are disabled for all device code.
+measurement aids ``calib/*.hip`` become ``libozcalib.so``, loaded only by bench.py.  Packed FP32 instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -17,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "liboz2.so")
-CALIB_SRC = os.path.join(PKG_DIR, "calib", "mfma_ceiling.hip")
+CALIB_DIR = os.path.join(PKG_DIR, "calib")
 CALIB_LIB = os.path.join(PKG_DIR, "libozcalib.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -57,10 +56,11 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
     tmp = CALIB_LIB + ".tmp"
-    cmd = [HIPCC, *COMMON_FLAGS, "-shared", "-o", tmp, CALIB_SRC]
+    calib_srcs = sorted(os.path.join(CALIB_DIR, f) for f in os.listdir(CALIB_DIR) if f.endswith(".hip"))
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", "-o", tmp, *calib_srcs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {CALIB_SRC}:\n{res.stderr}")
+        raise RuntimeError(f"hipcc failed for {calib_srcs}:\n{res.stderr}")
     os.replace(tmp, CALIB_LIB)
     if verbose:
         print(f"built {LIB_PATH} and {CALIB_LIB}", file=sys.stderr)
