@@ -110,6 +110,24 @@ def test_production_gemm_every_plane_in_full(oz, mode):
     log(f"[planes] production GEMM {mode}: ok")
 
 
+@pytest.mark.parametrize("p,q,r,s", [(2048, 300, 2048, 9), (2048, 300, 1536, 11)])
+def test_partial_last_round_every_plane_in_full(oz, p, q, r, s):
+    """Grids of the 8-wave kernel whose last round on a 256-CU device is partly empty:
+    576 tiles (s = 9, odd) and 528 tiles of a non-square product (s = 11).  Every R_t in
+    full, so tiles of the first and the last round, and of every plane, are all checked."""
+    import torch
+    assert big_tiles(p, r, s) >= 512 and 0 < big_tiles(p, r, s) % 256 <= 128
+    A = generate(p, q, 1.0, 511)
+    B = generate(q, r, 1.0, 512)
+    log(f"[planes] partial last round: p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, "fast", want=("d", "b", "R"))
+    torch.cuda.synchronize()
+    d, b, _ = oracle_exponents(A, B, s, "fast")
+    assert_equal(out["d"].cpu().numpy(), d.astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), b.astype(np.int32), "b")
+    _compare_planes(out, A, B, s, d, b, range(s), f"{p}x{q}x{r} s{s}")
+
+
 def test_headline_workload_planes_in_full(oz):
     """n = 8192 fast, s = 14: the m = 256 plane and an odd plane (m = 199) in full."""
     import torch
