@@ -64,8 +64,16 @@ Layout make_layout(int p, int q, int r, int s) {
   return L;
 }
 
+// Operands (A and B together) above this size are read with the non-temporal hint in the
+// statistics and residue passes: the 256 MB memory-side cache cannot keep them from one
+// pass to the next, and streamed reads that allocate there only evict the residue planes
+// and the other operand's tail.  Smaller operands are read normally, so the residue pass
+// finds them in that cache.
+constexpr double kStreamInputsBytes = 128.0 * (1 << 20);
+
 Work bind(const Layout& L, char* base, int p, int q, int r, int s, bool accu) {
   Work w{};
+  w.stream_inputs = 8.0 * (static_cast<double>(p) * q + static_cast<double>(q) * r) > kStreamInputsBytes;
   w.p = p;
   w.q = q;
   w.r = r;

@@ -43,6 +43,15 @@ __device__ __forceinline__ int exponent_of(double x) {
   return x == 0.0 ? kNoExp : __builtin_amdgcn_frexp_exp(x);
 }
 
+// Load of one FP64 input element; NT: with the non-temporal hint, for operands too large
+// for the memory-side cache to keep between the statistics and residue passes (streamed
+// reads then do not evict lines that would be reused).
+template <bool NT>
+__device__ __forceinline__ double load_f64(const double* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 __device__ __forceinline__ bool is_nonfinite(double x) {
   uint64_t bits = static_cast<uint64_t>(__double_as_longlong(x));
   return ((bits >> 52) & 0x7FFu) == 0x7FFu;

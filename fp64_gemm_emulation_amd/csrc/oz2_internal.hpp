@@ -15,6 +15,7 @@ struct Work {
   int p_pad, r_pad, q_pad;  // rows of A_t / B_t padded to kRowPad, inner dim to kKPad
   int nch;                  // number of kChunk-long blocks along q
   int tau;
+  bool stream_inputs;       // FP64 operand reads with the non-temporal hint (large operands)
   unsigned* flags;          // 1 word
   int* d;                   // [p]   row exponents of A
   int* b;                   // [r]   column exponents of B

@@ -149,7 +149,8 @@ struct ResidueOperand {
 // thread mapping owner_rows_of_a for workgroup (bx, by) (the thread's 16 elements of line i
 // are l = 256 blk + L + 16 k).  The validation dump of the scaled operand receives element
 // (line, l) at ap_dump[line dls + l dks].  A non-finite input (read as 0) sets the flag word.
-template <int S, int ND, bool DUMP>
+// NT: non-temporal reads of the operand (Work::stream_inputs).
+template <int S, int ND, bool DUMP, bool NT>
 __device__ __forceinline__ void residues_rows_block(const ResidueOperand& o, int q, int q_pad, int bx, int by,
                                                     unsigned* flags, double* ap_dump, long dls, long dks) {
   const ChunkOwner own = owner_rows_of_a(bx, by);
@@ -162,7 +163,7 @@ __device__ __forceinline__ void residues_rows_block(const ResidueOperand& o, int
   for (int k = 0; k < 16; ++k) {
     const int col = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = row_ok && col < q;
-    const double x = ok ? o.ptr[i + static_cast<long>(col) * o.ld] : 0.0;
+    const double x = ok ? load_f64<NT>(o.ptr + i + static_cast<long>(col) * o.ld) : 0.0;
     bad |= !__builtin_isfinite(x);
     double apv;
     g[k] = scaled_digits(x, scale, DUMP ? &apv : nullptr);
@@ -175,8 +176,8 @@ __device__ __forceinline__ void residues_rows_block(const ResidueOperand& o, int
 }
 
 // Contiguous lines (columns of B, or rows of op(A) = A^T); thread mapping owner_cols_of_b
-// for workgroup (bx, by).  Dump and flag as in residues_rows_block.
-template <int S, int ND, bool DUMP>
+// for workgroup (bx, by).  Dump, flag and NT as in residues_rows_block.
+template <int S, int ND, bool DUMP, bool NT>
 __device__ __forceinline__ void residues_cols_block(const ResidueOperand& o, int q, int q_pad, int bx, int by,
                                                     unsigned* flags, double* bp_dump, long dls, long dks) {
   const ChunkOwner own = owner_cols_of_b(bx, by);
@@ -190,7 +191,7 @@ __device__ __forceinline__ void residues_cols_block(const ResidueOperand& o, int
   for (int k = 0; k < 16; ++k) {
     const int row = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = col_ok && row < q;
-    const double x = ok ? col[row] : 0.0;
+    const double x = ok ? load_f64<NT>(col + row) : 0.0;
     bad |= !__builtin_isfinite(x);
     double bpv;
     g[k] = scaled_digits(x, scale, DUMP ? &bpv : nullptr);
@@ -203,28 +204,29 @@ __device__ __forceinline__ void residues_cols_block(const ResidueOperand& o, int
 }
 
 // One operand per launch (grid of its own thread mapping), with or without the dump.
-template <int S, int ND, bool DUMP, bool CONTIG>
+template <int S, int ND, bool DUMP, bool CONTIG, bool NT>
 __global__ __launch_bounds__(256) void residues_kernel(ResidueOperand o, int q, int q_pad, unsigned* __restrict__ flags,
                                                        double* __restrict__ dump, long dls, long dks) {
   if constexpr (CONTIG)
-    residues_cols_block<S, ND, DUMP>(o, q, q_pad, blockIdx.x, blockIdx.y, flags, dump, dls, dks);
+    residues_cols_block<S, ND, DUMP, NT>(o, q, q_pad, blockIdx.x, blockIdx.y, flags, dump, dls, dks);
   else
-    residues_rows_block<S, ND, DUMP>(o, q, q_pad, blockIdx.x, blockIdx.y, flags, dump, dls, dks);
+    residues_rows_block<S, ND, DUMP, NT>(o, q, q_pad, blockIdx.x, blockIdx.y, flags, dump, dls, dks);
 }
 
 // Both operands in one launch, for column-major A and B (the untransposed product): the
 // first nb_blocks workgroups take the columns of B (grid gxb wide), the rest the rows of A
 // (grid gxa wide).  One launch instead of two saves a dependent kernel start and the ramp
 // and tail of a second grid, which matter at small sizes.
-template <int S, int ND>
+template <int S, int ND, bool NT>
 __global__ __launch_bounds__(256) void residues_ab_kernel(ResidueOperand a, ResidueOperand b, int q, int q_pad,
                                                           int gxa, int gxb, int nb_blocks,
                                                           unsigned* __restrict__ flags) {
   const int k = blockIdx.x;
   if (k < nb_blocks)
-    residues_cols_block<S, ND, false>(b, q, q_pad, k % gxb, k / gxb, flags, nullptr, 0, 0);
+    residues_cols_block<S, ND, false, NT>(b, q, q_pad, k % gxb, k / gxb, flags, nullptr, 0, 0);
   else
-    residues_rows_block<S, ND, false>(a, q, q_pad, (k - nb_blocks) % gxa, (k - nb_blocks) / gxa, flags, nullptr, 0, 0);
+    residues_rows_block<S, ND, false, NT>(a, q, q_pad, (k - nb_blocks) % gxa, (k - nb_blocks) / gxa, flags, nullptr,
+                                          0, 0);
 }
 
 // Grid of one operand's residue launch: (lines / 16, q_pad / 256) for contiguous lines, else
@@ -234,18 +236,38 @@ static dim3 residue_grid(bool contig, int nlines_pad, int q_pad) {
 }
 
 // Residue planes of one operand (nlines_pad rows); dump element (line, l) at
-// dump[line dls + l dks].
-template <int S, int NL, bool DUMP>
+// dump[line dls + l dks] (the dumping kernels read normally: validation only).
+template <int S, int NL, bool DUMP, bool NT>
 static void residues_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, const int* scale,
                            int8_t* out, long plane, unsigned* flags, double* dump, long dls, long dks, hipStream_t st) {
+  static_assert(!(DUMP && NT), "dumping kernels read normally");
   const ResidueOperand ro{o.ptr, o.ld, nlines, scale, out, plane};
   const dim3 grid = residue_grid(o.contig, nlines_pad, q_pad);
   if (o.contig)
-    hipLaunchKernelGGL((residues_kernel<S, NL, DUMP, true>), grid, dim3(256), 0, st, ro, q, q_pad, flags, dump, dls,
-                       dks);
+    hipLaunchKernelGGL((residues_kernel<S, NL, DUMP, true, NT>), grid, dim3(256), 0, st, ro, q, q_pad, flags, dump,
+                       dls, dks);
   else
-    hipLaunchKernelGGL((residues_kernel<S, NL, DUMP, false>), grid, dim3(256), 0, st, ro, q, q_pad, flags, dump, dls,
-                       dks);
+    hipLaunchKernelGGL((residues_kernel<S, NL, DUMP, false, NT>), grid, dim3(256), 0, st, ro, q, q_pad, flags, dump,
+                       dls, dks);
+}
+
+template <int S, bool ACCU, bool NT>
+static void launch_residues_nt(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
+  constexpr int NL = digit_words(S, ACCU);
+  // untransposed operands: one launch for both (B's workgroups first: its statistics were
+  // the last pass over the inputs, measured 1-2% faster)
+  const dim3 ga = residue_grid(a.contig, w.p_pad, w.q_pad), gb = residue_grid(b.contig, w.r_pad, w.q_pad);
+  const long nb = static_cast<long>(gb.x) * gb.y, na = static_cast<long>(ga.x) * ga.y;
+  // (a one-dimensional grid keeps its work-item count below 2^32)
+  if (!a.contig && b.contig && nb + na < (1L << 24)) {
+    const ResidueOperand ra{a.ptr, a.ld, w.p, w.d, w.at, w.at_plane};
+    const ResidueOperand rb{b.ptr, b.ld, w.r, w.b, w.bt, w.bt_plane};
+    hipLaunchKernelGGL((residues_ab_kernel<S, NL, NT>), dim3(static_cast<unsigned>(nb + na)), dim3(256), 0, st, ra,
+                       rb, w.q, w.q_pad, static_cast<int>(ga.x), static_cast<int>(gb.x), static_cast<int>(nb), w.flags);
+    return;
+  }
+  residues_lines<S, NL, false, NT>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, w.flags, nullptr, 0L, 0L, st);
+  residues_lines<S, NL, false, NT>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, w.flags, nullptr, 0L, 0L, st);
 }
 
 template <int S, bool ACCU>
@@ -253,30 +275,27 @@ static void launch_residues_s(const Operand& a, const Operand& b, const Work& w,
                               hipStream_t st) {
   constexpr int NL = digit_words(S, ACCU);
   if (w.q_pad == 0) return;
-  // untransposed operands without dumps: one launch for both (B's workgroups first: its
-  // statistics were the last pass over the inputs, measured 1-2% faster)
-  const dim3 ga = residue_grid(a.contig, w.p_pad, w.q_pad), gb = residue_grid(b.contig, w.r_pad, w.q_pad);
-  const long nb = static_cast<long>(gb.x) * gb.y, na = static_cast<long>(ga.x) * ga.y;
-  // (a one-dimensional grid keeps its work-item count below 2^32)
-  if (!a.contig && b.contig && dump.ap == nullptr && dump.bp == nullptr && nb + na < (1L << 24)) {
-    const ResidueOperand ra{a.ptr, a.ld, w.p, w.d, w.at, w.at_plane};
-    const ResidueOperand rb{b.ptr, b.ld, w.r, w.b, w.bt, w.bt_plane};
-    hipLaunchKernelGGL((residues_ab_kernel<S, NL>), dim3(static_cast<unsigned>(nb + na)), dim3(256), 0, st, ra, rb,
-                       w.q, w.q_pad, static_cast<int>(ga.x), static_cast<int>(gb.x), static_cast<int>(nb), w.flags);
+  if (dump.ap == nullptr && dump.bp == nullptr) {
+    if (w.stream_inputs)
+      launch_residues_nt<S, ACCU, true>(a, b, w, st);
+    else
+      launch_residues_nt<S, ACCU, false>(a, b, w, st);
     return;
   }
   // A' dump: column-major p x q (ld p); B' dump: column-major q x r (ld q); each operand
   // runs the dumping kernel only when its own dump is requested
   if (dump.bp != nullptr)
-    residues_lines<S, NL, true>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, w.flags, dump.bp,
-                                static_cast<long>(w.q), 1L, st);
+    residues_lines<S, NL, true, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, w.flags, dump.bp,
+                                       static_cast<long>(w.q), 1L, st);
   else
-    residues_lines<S, NL, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, w.flags, nullptr, 0L, 0L, st);
+    residues_lines<S, NL, false, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, w.flags, nullptr, 0L,
+                                        0L, st);
   if (dump.ap != nullptr)
-    residues_lines<S, NL, true>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, w.flags, dump.ap, 1L,
-                                static_cast<long>(w.p), st);
+    residues_lines<S, NL, true, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, w.flags, dump.ap, 1L,
+                                       static_cast<long>(w.p), st);
   else
-    residues_lines<S, NL, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, w.flags, nullptr, 0L, 0L, st);
+    residues_lines<S, NL, false, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.d, w.at, w.at_plane, w.flags, nullptr, 0L,
+                                        0L, st);
 }
 
 template <int S>

@@ -43,7 +43,7 @@ constexpr int kStatsRowGroups = 1;
 constexpr int kStatsColGroups = 8;
 constexpr int kStatsCols = kChunk / kStatsColGroups;
 constexpr int kStatsThreads = kWave * kStatsRowGroups * kStatsColGroups;
-template <bool MAXONLY>
+template <bool MAXONLY, bool NT>
 __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double* __restrict__ A, long lda, int p,
                                                                    int q, int nch, int* __restrict__ part_e,
                                                                    double* __restrict__ part_s,
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
 #pragma unroll
   for (int k = 0; k < kStatsCols; ++k) {
     double x = 0.0;
-    if (row_ok && l0 + k < q) x = base[static_cast<long>(k) * lda];
+    if (row_ok && l0 + k < q) x = load_f64<NT>(base + static_cast<long>(k) * lda);
     x = is_nonfinite(x) ? 0.0 : x;  // (flagged by the residue stage)
     v[k] = x;
     emax = max(emax, exponent_of(x));
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kStatsThreads) void stats_rows_kernel(const double*
 // are issued before the first block is reduced.  CB = 2 where lines have at most 32
 // blocks (more waves in flight on small grids), else 8 (one wave per block made 65536 tiny
 // workgroups at n = 8192, which the dispatcher could not launch fast enough).
-template <bool MAXONLY, int CB>
+template <bool MAXONLY, int CB, bool NT>
 __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restrict__ B, long ldb, int q, int r,
                                                          int nch, int* __restrict__ part_e,
                                                          double* __restrict__ part_s,
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int l = (c0 + b) * kChunk + lane + kWave * k;
-      const double x = (col_ok && c0 + b < nch && l < q) ? col[l] : 0.0;
+      const double x = (col_ok && c0 + b < nch && l < q) ? load_f64<NT>(col + l) : 0.0;
       v[b][k] = is_nonfinite(x) ? 0.0 : x;  // (flagged by the residue stage)
     }
 #pragma unroll
@@ -348,9 +348,10 @@ hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st
 }
 
 // Block statistics of the lines of one operand (rows of op(A) or columns of op(B)).
-template <bool MAXONLY>
 // With qout (accu), the block-quantized bound input of every line up to nlines_pad is written
-// too (zeros past nlines), in the operand tile layout of q_pad columns.
+// too (zeros past nlines), in the operand tile layout of q_pad columns.  NT: non-temporal
+// reads of the operand (Work::stream_inputs).
+template <bool MAXONLY, bool NT>
 static void stats_lines(const Operand& o, int nlines, int nlines_pad, int q, int q_pad, int nch, int* pe, double* ps,
                         int8_t* qout, hipStream_t st) {
   if (nch == 0 || nlines == 0) return;
@@ -358,17 +359,17 @@ static void stats_lines(const Operand& o, int nlines, int nlines_pad, int q, int
   if (o.contig) {
     if (nch <= 32) {
       dim3 grid(ngrid, blocks_for(nch, 4 * 2));
-      hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 2>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps,
-                         qout, q_pad);
+      hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 2, NT>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe,
+                         ps, qout, q_pad);
     } else {
       dim3 grid(ngrid, blocks_for(nch, 4 * 8));
-      hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 8>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe, ps,
-                         qout, q_pad);
+      hipLaunchKernelGGL((stats_cols_kernel<MAXONLY, 8, NT>), grid, dim3(256), 0, st, o.ptr, o.ld, q, nlines, nch, pe,
+                         ps, qout, q_pad);
     }
   } else {
     dim3 grid(blocks_for(ngrid, kWave * kStatsRowGroups), nch);
-    hipLaunchKernelGGL(stats_rows_kernel<MAXONLY>, grid, dim3(kStatsThreads), 0, st, o.ptr, o.ld, nlines, q, nch, pe,
-                       ps, qout, q_pad);
+    hipLaunchKernelGGL((stats_rows_kernel<MAXONLY, NT>), grid, dim3(kStatsThreads), 0, st, o.ptr, o.ld, nlines, q, nch,
+                       pe, ps, qout, q_pad);
   }
 }
 
@@ -376,8 +377,13 @@ template <bool MAXONLY>
 static hipError_t launch_stats(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
   int8_t* const qa = MAXONLY ? w.abar : nullptr;
   int8_t* const qb = MAXONLY ? w.bbar : nullptr;
-  stats_lines<MAXONLY>(a, w.p, w.p_pad, w.q, w.q_pad, w.nch, w.part_e_a, w.part_s_a, qa, st);
-  stats_lines<MAXONLY>(b, w.r, w.r_pad, w.q, w.q_pad, w.nch, w.part_e_b, w.part_s_b, qb, st);
+  if (w.stream_inputs) {
+    stats_lines<MAXONLY, true>(a, w.p, w.p_pad, w.q, w.q_pad, w.nch, w.part_e_a, w.part_s_a, qa, st);
+    stats_lines<MAXONLY, true>(b, w.r, w.r_pad, w.q, w.q_pad, w.nch, w.part_e_b, w.part_s_b, qb, st);
+  } else {
+    stats_lines<MAXONLY, false>(a, w.p, w.p_pad, w.q, w.q_pad, w.nch, w.part_e_a, w.part_s_a, qa, st);
+    stats_lines<MAXONLY, false>(b, w.r, w.r_pad, w.q, w.q_pad, w.nch, w.part_e_b, w.part_s_b, qb, st);
+  }
   return hipGetLastError();
 }
 
