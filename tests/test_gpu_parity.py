@@ -40,7 +40,8 @@ def test_workload_n256_fast_s8_full(oz):
 
 
 @pytest.mark.parametrize("mode", ["fast", "accu"])
-@pytest.mark.parametrize("shape", [(300, 517, 129), (1, 1, 1), (257, 256, 255), (513, 1000, 70), (5, 2049, 3)])
+@pytest.mark.parametrize("shape", [(300, 517, 129), (1, 1, 1), (257, 256, 255), (513, 1000, 70), (5, 2049, 3),
+                                   (70, 9000, 45)])
 def test_ragged_shapes(oz, mode, shape):
     p, q, r = shape
     A = generate(p, q, 1.0, 11 + p)
