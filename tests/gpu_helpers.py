@@ -70,16 +70,20 @@ def compare_full(out, ref, A, B, s, mode):
         assert_equal(out["Bbar"].cpu().numpy(), ref["Bbar"].astype(np.int8), "Bbar")
         assert_equal(out["rho"].cpu().numpy(), ref["rho"].astype(np.int32), "rho")
         assert_equal(out["gamma"].cpu().numpy(), ref["gamma"].astype(np.int32), "gamma")
-    assert_equal(out["Ap"].cpu().numpy(), ref["Ap"], "A'")
-    assert_equal(out["Bp"].cpu().numpy(), ref["Bp"], "B'")
+    # A' and B' are dumped only when requested; the residue stage then runs the kernel form
+    # that writes them, so runs without them check the production residue kernels' A_t, B_t
+    if "Ap" in out:
+        assert_equal(out["Ap"].cpu().numpy(), ref["Ap"], "A'")
+        assert_equal(out["Bp"].cpu().numpy(), ref["Bp"], "B'")
     at = out["At"].cpu().numpy()
     bt = out["Bt"].cpu().numpy()
-    pt = out["P"].cpu().numpy()
+    pt = out["P"].cpu().numpy() if "P" in out else None
     rt = out["R"].cpu().numpy()
     for t in range(s):
         assert_equal(at[t], ref["At"][t].astype(np.int8), f"A_t t={t}")
         assert_equal(bt[t], ref["Bt"][t].T.astype(np.int8), f"B_t t={t}")
-        assert_equal(pt[t], ref["P"][t].T.astype(np.int32), f"P_t t={t}")
+        if pt is not None:
+            assert_equal(pt[t], ref["P"][t].T.astype(np.int32), f"P_t t={t}")
         assert_equal(rt[t], ref["R"][t].T.astype(np.uint8), f"R_t t={t}")
     xg = out["X"].cpu().numpy()
     for j in range(r):
@@ -105,10 +109,11 @@ def compare_sampled(out, ref, A, B, s, mode, rows, cols):
         assert np.array_equal(out["gamma"][cols_t].cpu().numpy(), ref["gamma"].astype(np.int32)), "gamma"
         assert np.array_equal(out["Abar"][rows_t].cpu().numpy(), ref["Abar"].astype(np.int8)), "Abar"
         assert np.array_equal(out["Bbar"][cols_t].cpu().numpy(), ref["Bbar"].astype(np.int8)), "Bbar"
-    ap = out["Ap"][rows_t].cpu().numpy()
-    bp = out["Bp"][:, cols_t].cpu().numpy()
-    assert_equal(ap, ref["Ap"], "A'")
-    assert_equal(bp, ref["Bp"], "B'")
+    if "Ap" in out:
+        ap = out["Ap"][rows_t].cpu().numpy()
+        bp = out["Bp"][:, cols_t].cpu().numpy()
+        assert_equal(ap, ref["Ap"], "A'")
+        assert_equal(bp, ref["Bp"], "B'")
     at = out["At"][:, rows_t, :].cpu().numpy()
     bt = out["Bt"][:, cols_t, :].cpu().numpy()
     # P_t is dumped only when requested; the GEMM launch then runs the kernel form that

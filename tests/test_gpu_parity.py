@@ -160,6 +160,36 @@ def _block_spread(rows, q, seed):
     return X
 
 
+@pytest.mark.parametrize("s", [14, 18])
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_lines_near_the_scaled_bound(oz, mode, s):
+    """Lines whose mass sits in one element are scaled up to |A'| near the bound 2^(tau/2),
+    beside dense lines several bits below it, through the production residue kernels (no
+    A' / B' dump).  d, b, A_t, B_t, R_t, X (and accu's e, f, rho, gamma, Abar, Bbar)
+    bit-exact and C within tolerance, in full."""
+    p, q, r = 200, 700, 150
+    A = generate(p, q, 0.5, 71 + s)
+    B = generate(q, r, 0.5, 72 + s)
+    for i in (0, 37, 150, 199):
+        A[i, (5 * i) % q] = 1e6
+    A[198, :] = 0.0  # a single nonzero element: the scaled line reaches the bound itself
+    A[198, 3] = 7e5
+    for j in (3, 90, 149):
+        B[(7 * j) % q, j] = -3e5
+    # no A' / B' dump: the production residue kernels run, and their A_t, B_t are compared
+    label = f"near-bound s{s} {mode}"
+    log(f"[full] {label}: p,q,r={p},{q},{r}")
+    want = ("d", "b", "At", "Bt", "R", "X") + (("e", "f", "rho", "gamma", "Abar", "Bbar") if mode == "accu" else ())
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=want)
+    ref = oracle.ozaki2(A, B, s, mode)
+    compare_full(out, ref, A, B, s, mode)
+    # the dominant lines reach |A'| >= 2^53, where the second digit word of the residue
+    # kernels carries nonzero digits
+    top_a = out["d"].cpu().numpy().astype(np.int64) + np.frexp(np.abs(A).max(axis=1))[1]
+    assert top_a.max() >= 54, int(top_a.max())
+    log(f"[full] {label}: ok")
+
+
 @pytest.mark.parametrize("mode", ["fast", "accu"])
 def test_block_exponent_spread(oz, mode):
     """Blocks of one line far apart in scale: the block exponents, the accu bound inputs
