@@ -70,6 +70,8 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ re
   }
   const int bj = b[j];
   double out[kRowsPerThread];
+  int scale[kRowsPerThread];
+  int smin = 0;
 #pragma unroll
   for (int v = 0; v < kRowsPerThread; ++v) {
     const int i = min(i0 + v, p - 1);  // rows past p (last group only) are computed, not stored
@@ -82,7 +84,17 @@ __global__ __launch_bounds__(256) void crt_kernel(const uint8_t* __restrict__ re
 #pragma unroll
       for (int k = 0; k < 5; ++k) xd[k] = wd[k];
     }
-    out[v] = crt_round<L, CrtTable<S>::kW, CrtTable<S>::kTopExp>(acc[v], -(d[i] + bj));
+    scale[v] = -(d[i] + bj);
+    smin = min(smin, scale[v]);
+    out[v] = ldexp(crt_round53<L, CrtTable<S>::kW, CrtTable<S>::kTopExp>(acc[v]), scale[v]);
+  }
+  // ldexp(RN53(X), scale) is RN(X 2^scale) unless the result falls below 2^-1022 with
+  // scale < -1074 (crt_round); only threads with such a scale take that path, so the
+  // common path stays short and its code compact.
+  if (smin < -1074) {
+#pragma unroll
+    for (int v = 0; v < kRowsPerThread; ++v)
+      out[v] = crt_round<L, CrtTable<S>::kW, CrtTable<S>::kTopExp>(acc[v], scale[v]);
   }
   double* dst = C + i0 + static_cast<long>(j) * ldc;
   if (beta != 0.0) {

@@ -146,6 +146,25 @@ def test_headline_workload_planes_in_full(oz):
     torch.cuda.empty_cache()
 
 
+def test_largest_workload_planes_in_full(oz):
+    """n = 16384 fast, s = 18 (256 stages of the inner dimension per tile, the longest
+    K loop of the five workloads): d and b, the m = 256 plane and the last odd plane
+    (m = 181) in full."""
+    import torch
+    w = WORKLOADS["n16384_fast_s18"]
+    A, B = w.inputs()
+    log(f"[planes] {w.name}: GPU run")
+    out = oz.dgemm_debug(to_device(A), to_device(B), w.s, w.mode, want=("d", "b", "R"))
+    torch.cuda.synchronize()
+    log(f"[planes] {w.name}: oracle exponents")
+    d, b, _ = oracle_exponents(A, B, w.s, w.mode)
+    assert_equal(out["d"].cpu().numpy(), d.astype(np.int32), "d")
+    assert_equal(out["b"].cpu().numpy(), b.astype(np.int32), "b")
+    _compare_planes(out, A, B, w.s, d, b, [0, w.s - 1], w.name)
+    del out
+    torch.cuda.empty_cache()
+
+
 def test_accu_workload_scalings_in_full(oz):
     """n = 8192 accu, s = 14 (bound GEMM on the 8-wave kernel with its row / column maximum
     epilogue): e, f, rho, gamma, d and b in full, and one residue plane (m = 233) in full."""
