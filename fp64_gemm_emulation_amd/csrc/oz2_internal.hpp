@@ -55,8 +55,6 @@ struct DumpPtrs {
 };
 
 // scaling stage
-hipError_t launch_fill_i32(int* ptr, int value, long n, hipStream_t st);
-hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st);
 hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w, hipStream_t st);
 hipError_t launch_accu_bound_inputs(const Operand& a, const Operand& b, const Work& w, hipStream_t st);
 hipError_t launch_accu_exponents(const Work& w, hipStream_t st);

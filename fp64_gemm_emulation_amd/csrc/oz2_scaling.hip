@@ -24,16 +24,6 @@
 
 namespace oz2 {
 
-__global__ void fill_i32_kernel(int* __restrict__ p, int v, long n) {
-  long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-__global__ void fill_u32_kernel(unsigned* __restrict__ p, unsigned v, long n) {
-  long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
 // Lines that are rows of a column-major matrix (rows of A, or columns of op(B) = B^T):
 // kStatsRowGroups x 64 lines (one per lane) x one kChunk block per workgroup; the
 // kStatsColGroups waves of a row group split the block's columns, wave w reading
@@ -376,18 +366,6 @@ __global__ void accu_exponents_kernel(int na, int nb, const int* __restrict__ e_
 // Host launchers
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(long n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
-
-hipError_t launch_fill_i32(int* ptr, int value, long n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, ptr, value, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_u32(unsigned* ptr, unsigned value, long n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, ptr, value, n);
-  return hipGetLastError();
-}
 
 // Block statistics of the lines of one operand (rows of op(A) or columns of op(B)).
 // With qout (accu), the block-quantized bound input of every line up to nlines_pad is written
