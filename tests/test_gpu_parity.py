@@ -407,6 +407,42 @@ def test_workload_n16384_accu_s18(oz):
     _sampled_case(oz, "n16384_accu_s18", nsamp=8)
 
 
+@pytest.mark.parametrize("mode", ["fast", "accu"])
+def test_edge_values_on_the_production_path(oz, mode):
+    """The edge values of test_edge_values in a product large enough for the production
+    path: 3072 x 3000 x 3072 (A and B above 128 MiB, so the statistics and residue passes
+    read them non-temporally; 2016 tiles on the 8-wave GEMM), no A' / B' dump (the
+    production residue kernels run).  The special rows and columns and a sample of the
+    others are compared with the oracle, d and b in full."""
+    import torch
+    p, q, r, s = 3072, 3000, 3072, 14
+    A = generate(p, q, 4.0, 15)
+    B = generate(q, r, 4.0, 16)
+    A[3, :] = 0.0                           # zero row
+    B[:, 7] = 0.0                           # zero column
+    A[5, 10] = 5e-324                       # subnormals
+    A[6, :20] = -3e-310
+    A[2900, :] = 5e-320
+    B[11, 2] = 1e300                        # huge
+    B[12, 3] = -1e-300
+    A[9, :] = 1.0                           # flat row
+    A[1800, 77] = 1e200                     # one dominant element
+    want = ("d", "b", "At", "Bt", "R", "X") + (("rho", "gamma", "Abar", "Bbar") if mode == "accu" else ())
+    log(f"[edges, production path] mode={mode} p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(to_device(A), to_device(B), s, mode, want=want)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(sample_indices(p, 8, 13).tolist()) | {3, 5, 6, 9, 1800, 2900, 3071}))
+    cols = np.array(sorted(set(sample_indices(r, 8, 14).tolist()) | {2, 3, 7, 3071}))
+    ref = oracle.ozaki2_sample(A, B, s, mode, rows, cols)
+    compare_sampled(out, ref, A, B, s, mode, rows, cols)
+    if mode == "fast":
+        d_ref, _, _ = oracle.fast_exponents(A, s)
+        b_ref, _, _ = oracle.fast_exponents(np.asarray(B).T, s)
+        assert np.array_equal(out["d"].cpu().numpy(), d_ref.astype(np.int32)), "d"
+        assert np.array_equal(out["b"].cpu().numpy(), b_ref.astype(np.int32)), "b"
+    log("[edges, production path] ok")
+
+
 @pytest.mark.parametrize("raw_p", [False, True])
 @pytest.mark.parametrize("mode", ["fast", "accu"])
 def test_large_tiles_on_ragged_shape(oz, mode, raw_p):
