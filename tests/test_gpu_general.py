@@ -54,6 +54,36 @@ def test_transposed_operands(oz, mode, ta, tb):
     log(f"[ex] ok ({int(np.sum(c_ex != ref['C']))} entries differ from the correctly rounded value)")
 
 
+@pytest.mark.parametrize("mode,ta,tb", [("fast", True, False), ("fast", False, True), ("fast", True, True),
+                                        ("accu", True, True)])
+def test_transposed_operands_on_the_production_path(oz, mode, ta, tb):
+    """3072 x 3000 x 2560, s = 14: A and B above 128 MiB (non-temporal reads in the
+    statistics and residue passes, whose row and column kernels swap roles for transposed
+    operands) and 1680 tiles on the 8-wave GEMM.  ozaki2_dgemm_ex must equal ozaki2_dgemm
+    on explicit copies of op(A), op(B) bit for bit, and sampled entries must match the
+    oracle."""
+    import torch
+    from tests.gpu_helpers import sample_indices
+    p, q, r, s = 3072, 3000, 2560, 14
+    opA = generate(p, q, 1.0, 43)
+    opB = generate(q, r, 1.0, 44)
+    log(f"[ex large] transa={ta} transb={tb} mode={mode} p,q,r={p},{q},{r}")
+    A_stored = to_device(np.ascontiguousarray(opA.T) if ta else opA)
+    B_stored = to_device(np.ascontiguousarray(opB.T) if tb else opB)
+    c_ex = oz.dgemm_ex(A_stored, B_stored, transa=ta, transb=tb, s=s, mode=mode)
+    del A_stored, B_stored
+    c_plain = oz.dgemm(to_device(opA), to_device(opB), s, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(c_ex, c_plain), "ozaki2_dgemm_ex vs ozaki2_dgemm on op(A), op(B)"
+    rows = sample_indices(p, 10, 21)
+    cols = sample_indices(r, 10, 22)
+    ref = oracle.ozaki2_sample(opA, opB, s, mode, rows, cols)
+    c = c_ex.cpu().numpy()[np.ix_(rows, cols)]
+    assert_chat_close(c, ref["C"], chat_tolerance(opA, opB, rows, cols), "C")
+    assert_correctly_rounded(c, ref["C"], "C")
+    log("[ex large] ok")
+
+
 @pytest.mark.parametrize("mode", ["fast", "accu"])
 @pytest.mark.parametrize("alpha,beta", [(-0.75, 1.5), (2.0, 0.0), (1.0, -1.0), (0.0, 0.5)])
 def test_alpha_beta(oz, mode, alpha, beta):
