@@ -51,10 +51,10 @@ __global__ __launch_bounds__(256, BT == 256 ? 1 : 2) void gemm_w4_kernel(
   tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
   const int i0 = tile_i * BT;
   const int j0 = tile_j * BT;
-  ModRed mr{0, 0, 0, 0.0f, 0.0f};
+  ModRed mr{0, 0, 0.0, 0.0};
   if constexpr (EPI != kEpiBound) {
     mr = kModRed[t];
-    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
+    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.inv), "+s"(mr.magic));
   }
   // Copies: the tile's rows i0 .. i0 + BT - 1 are contiguous in each 16 KiB stage tile of
   // their 256-row block, from byte 64 (i0 mod 256); wave w moves bytes [(kSlice/2)(w mod 2)

@@ -64,20 +64,20 @@ static_assert(kStages == 4, "the copy schedule and its wait counts assume a ring
 
 // Constants of the output reduction R = P mod m for each modulus (index t).  The
 // accumulators start at -h (h = (m - 1) / 2 for odd m, 0 for m = 256), so the epilogue
-// sees P' = P - h:
-//   z = (P' mod 2^16) + (P' >> 16) c16 with c16 the centered residue of 2^16, computed as
-//       one v_mad_i32_i24 with the multiplier c16 - 2^16; |z| < 2^22.02 and z = P' (mod m);
-//   y = RN(z / m + magic) in FP32 gives magic + round(z / m) exactly (z / m is never within
-//       1/(2m) of a half-integer and the FP32 quotient is within 0.26/m of it);
-//   z - m (low 24 bits of y) = [z - m round(z / m)] - m 2^22 + m e, and with
-//       magic = 1.5 2^23 - e, e = h m^-1 (mod 256), its low byte is
-//       centered residue of P' + h = P mod m, in [0, m).
+// sees P' = P - h with |P'| < 2^31:
+//   y = RN(P' inv + magic) in FP64, inv = RN(1 / m), magic = 1.5 2^52 - e, is exactly
+//       magic + round(P' / m): P' inv lies within 2^-22 / m of P' / m, which for odd m is
+//       never closer than 1 / (2m) to a half-integer, and the sum stays in [2^52, 2^53);
+//   the low 32 bits of y are then round(P' / m) - e (mod 2^32), and one v_mad_i32_i24
+//       gives P' - m (round(P' / m) - e) (mod 2^24), whose low byte, with
+//       e = h m^-1 (mod 256), is the centered residue of P' plus h = P mod m, in [0, m).
+// Three VALU operations per output (convert, FMA, multiply-add), all at the full vector
+// rate: CDNA4 issues FP64 FMAs as fast as unpacked FP32 ones.
 struct ModRed {
   int m;
   int h;
-  int c16m;      // centered (2^16 mod m) - 2^16
-  float inv;     // RN(1 / m)
-  float magic;   // 1.5 2^23 - e
+  double inv;    // RN(1 / m)
+  double magic;  // 1.5 2^52 - e
 };
 
 constexpr int half_of(int m) { return (m & 1) ? (m - 1) / 2 : 0; }
@@ -86,9 +86,8 @@ constexpr int shift_e(int m) {
                  : 0;
 }
 constexpr ModRed mod_red(int t) {
-  return ModRed{modulus(t), half_of(modulus(t)),
-                centered_small(pow2_mod(16, static_cast<uint32_t>(modulus(t))), static_cast<uint32_t>(modulus(t))) - 65536,
-                1.0f / static_cast<float>(modulus(t)), 12582912.0f - static_cast<float>(shift_e(modulus(t)))};
+  return ModRed{modulus(t), half_of(modulus(t)), 1.0 / static_cast<double>(modulus(t)),
+                6755399441055744.0 - static_cast<double>(shift_e(modulus(t)))};
 }
 constexpr bool mod_red_ok() {
   for (int t = 0; t < kMaxS; ++t) {
@@ -112,9 +111,8 @@ __device__ __forceinline__ int mad_i24(int a, int b, int c) {
 
 // Low byte = P mod m for an accumulator holding P' = P - h (odd m); see ModRed.
 __device__ __forceinline__ uint32_t mod_byte(int pp, const ModRed& mr) {
-  const int z = mad_i24(pp >> 16, mr.c16m, pp);
-  const float y = __builtin_fmaf(static_cast<float>(z), mr.inv, mr.magic);
-  return static_cast<uint32_t>(mad_i24(__float_as_int(y), -mr.m, z));
+  const double y = __builtin_fma(static_cast<double>(pp), mr.inv, mr.magic);
+  return static_cast<uint32_t>(mad_i24(static_cast<int>(__double_as_longlong(y)), -mr.m, pp));
 }
 
 // Residue bytes of the four rows held in accumulator registers 4 g .. 4 g + 3 of one
@@ -255,10 +253,10 @@ __global__ __launch_bounds__(256, TB == 4 ? 1 : 2) void gemm_i8_kernel(
   // Accumulators start at -h for the mod epilogues (see ModRed), at 0 for the bound.
   // The modulus constants are loaded here and pinned in scalar registers: loaded in the
   // epilogue, their latency would stall every wave at the end of every tile.
-  ModRed mr{0, 0, 0, 0.0f, 0.0f};
+  ModRed mr{0, 0, 0.0, 0.0};
   if constexpr (EPI != kEpiBound) {
     mr = kModRed[t];
-    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
+    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.inv), "+s"(mr.magic));
   }
   const int init = -mr.h;
   v16i acc[TB][TB];
@@ -513,10 +511,10 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
   tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
   const int i0 = tile_i * BT;
   const int j0 = tile_j * BT;
-  ModRed mr{0, 0, 0, 0.0f, 0.0f};
+  ModRed mr{0, 0, 0.0, 0.0};
   if constexpr (EPI != kEpiBound) {
     mr = kModRed[t];
-    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.c16m), "+s"(mr.inv), "+s"(mr.magic));
+    asm volatile("" : "+s"(mr.m), "+s"(mr.h), "+s"(mr.inv), "+s"(mr.magic));
   }
 
   // Copies: waves 0-3 move the A slice, waves 4-7 the B slice; wave w moves bytes
@@ -578,11 +576,15 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
       stage(kt, x0, x1);
       stage(kt + 1, x1, x0);
     }
-    OZ2_WAIT_VMCNT(0);
+    // Copies still in flight now are at most those issued in the last two stages, into the
+    // buffers of stages nk - 2 and nk - 1; the mod epilogue stages its residues through the
+    // other two and waits for these only after that.
+    OZ2_WAIT_VMCNT(2 * kCopiesW);
     OZ2_WAIT_LGKMCNT(0);
   }
 
   if constexpr (EPI == kEpiBound) {
+    OZ2_WAIT_VMCNT(0);
     // rows: max over this wave's 4 column blocks, then over the 16 lanes of each row group
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -612,9 +614,11 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
     }
     return;
   }
-  // Epilogue: residue words through the (now free) LDS ring as in gemm_i8_kernel, so that
-  // every store instruction writes whole 256-byte column segments.
+  // Epilogue: residue words through the first two stage buffers of the LDS ring (those of
+  // stages nk - 4 and nk - 3, whose copies have landed) as in gemm_i8_kernel, so that every
+  // store instruction writes whole 256-byte column segments.
   constexpr int WC = BT / 4;
+  static_assert(BT * BT <= 2 * kStageLds, "staging fits the first two stage buffers");
   uint32_t* const stg = reinterpret_cast<uint32_t*>(smem);
   __builtin_amdgcn_s_barrier();
   const int jl0 = wn * 64 + (lane & 15);
@@ -633,17 +637,27 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
     stage_all(std::true_type{});
   else
     stage_all(std::false_type{});
+  // the last copies have landed before anything leaves the LDS ring (and before the
+  // workgroup's LDS can be released); no global store is in flight yet
+  OZ2_WAIT_VMCNT(0);
   __syncthreads();
   uint8_t* const rt = res + t * r_plane;
   constexpr int kTpc = BT / 16;                // threads per column
   constexpr int kCols = 512 / kTpc;            // columns per pass
+  constexpr int kPasses = BT / kCols;
   const int c = tid % kTpc;
-#pragma unroll 4
-  for (int pass = 0; pass < BT / kCols; ++pass) {
+  // all reads first: their latencies overlap instead of preceding one store each
+  v4i d[kPasses];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int jl = pass * kCols + tid / kTpc;
-    const v4i d = *reinterpret_cast<const v4i*>(stg + WC * jl + 4 * (c ^ ((jl & 31) >> 2)));
+    d[pass] = *reinterpret_cast<const v4i*>(stg + WC * jl + 4 * (c ^ ((jl & 31) >> 2)));
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int jl = pass * kCols + tid / kTpc;
     const int sw = jl & 3;
-    int x0w = d[0], x1w = d[1], x2w = d[2], x3w = d[3];
+    int x0w = d[pass][0], x1w = d[pass][1], x2w = d[pass][2], x3w = d[pass][3];
     if (sw & 1) {
       const int y0 = x0w, y2 = x2w;
       x0w = x1w; x1w = y0; x2w = x3w; x3w = y2;
