@@ -2,7 +2,9 @@
 
 Each ``csrc/*.hip`` file is compiled to an object with hipcc in parallel, then the
 objects are linked into ``fp64_gemm_emulation_amd/liboz2.so`` (the library).  The
-measurement aids ``calib/*.hip`` become ``libozcalib.so``, loaded only by bench.py.  Packed FP32 instructions are disabled for all device code.
+measurement aids ``calib/*.hip`` become ``libozcalib.so``, loaded by bench.py and by the
+GPU test that drives the GEMM epilogue with chosen operand planes; the product path never
+loads it.  Packed FP32 instructions are disabled for all device code.
 """
 from __future__ import annotations
 
