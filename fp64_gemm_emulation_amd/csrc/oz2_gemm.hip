@@ -504,8 +504,14 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2;                    // rows 128 wm
-  const int wn = wave & 3;                     // columns 64 wn
+  // Waves w and w + 4 share a SIMD (waves go to SIMDs round-robin) and interleave their
+  // MFMAs there; giving them the same 128 rows (wm) and different columns lets the A
+  // operand the matrix core sees stay unchanged across both waves' MFMAs of one block row.
+  // Under the board's power limit, fewer operand bits switching per MFMA is clock: with the
+  // block order below, 1.3% shorter GEMM stage than partners sharing columns with a
+  // row-major order (n = 8192, s = 14).
+  const int wm = wave & 1;                     // rows 128 wm
+  const int wn = wave >> 1;                    // columns 64 wn
   const int t = blockIdx.z;
   int tile_i, tile_j;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tile_i, tile_j);
@@ -552,7 +558,9 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(const int8_t* __restric
     const int kn = min(kt + kStages, nk - 1);
 #pragma unroll
     for (int u = 0; u < MB * NB; ++u) {
-      const int mb = u / NB, nb = u % NB;
+      // block rows in order, the columns of every other row reversed (a snake): each step
+      // changes one operand fragment, and the B fragment stays across a row change
+      const int mb = u / NB, nb = (mb & 1) ? NB - 1 - u % NB : u % NB;
       acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x[mb], x[MB + nb], acc[mb][nb], 0, 0, 0);
       if (u % 2 == 1 && u / 2 < kFr) read1(kt + 1, y, u / 2);
       if (u % 8 == 4) copy1(kt, kn, u / 8);
