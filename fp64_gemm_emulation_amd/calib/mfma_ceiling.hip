@@ -46,18 +46,25 @@ __global__ __launch_bounds__(512, 1) void mfma_i8_ceiling_kernel(const v4i* __re
 
 // The same instruction in the exact shape of the large-grid mod GEMM: one workgroup of 8
 // waves per 256 x 256 output tile (the GEMM's grid), each wave 8 x 4 blocks of 16 x 16 (32
-// accumulators) issued in the GEMM's order, and 12 fragments (8 of A, 4 of B) that all change
-// after every 32 MFMAs, as the GEMM reads new fragments for every 64-deep stage.  128 KiB of
-// LDS is held (never touched) so that one workgroup runs per CU, as for the GEMM.  What it
-// leaves out is the GEMM's memory traffic (copies into LDS, fragment reads) and its
+// accumulators) issued in the GEMM's order (block rows in turn, every other row's columns
+// reversed), and 12 fragments (8 of A, 4 of B) that all change after every 32 MFMAs, as the
+// GEMM reads new fragments for every 64-deep stage.  As in the GEMM, the waves of one row
+// half (wave & 1) hold the same A fragments and the waves of one column quarter (wave >> 1)
+// the same B fragments, so the two waves that share a SIMD (w, w + 4) see the same A.
+// 128 KiB of LDS is held (never touched) so that one workgroup runs per CU, as for the GEMM.
+// What it leaves out is the GEMM's memory traffic (copies into LDS, fragment reads) and its
 // epilogue, so the GEMM's rate over this one's is the cost of those at equal MFMA work.
 __global__ __launch_bounds__(512, 1) void mfma_i8_gemm_shape_kernel(const v4i* __restrict__ src, int stages,
                                                                       int* __restrict__ out) {
   __shared__ int lds_hold[128 * 1024 / 4];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
   v4i f[12];
 #pragma unroll
-  for (int g = 0; g < 12; ++g) f[g] = src[((blockIdx.x & 1023) * 12 + g) * 512 + tid];
+  for (int g = 0; g < 12; ++g)
+    f[g] = src[((blockIdx.x & 1023) * 12 + g) * 512 + (g < 8 ? wm : 2 + wn) * 64 + lane];
   v4i acc[8][4];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb)
@@ -65,10 +72,10 @@ __global__ __launch_bounds__(512, 1) void mfma_i8_gemm_shape_kernel(const v4i* _
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = v4i{};
   for (int kt = 0; kt < stages; ++kt) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[mb], f[8 + nb], acc[mb][nb], 0, 0, 0);
+    for (int u = 0; u < 32; ++u) {
+      const int mb = u / 4, nb = (mb & 1) ? 3 - u % 4 : u % 4;
+      acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[mb], f[8 + nb], acc[mb][nb], 0, 0, 0);
+    }
 #pragma unroll
     for (int g = 0; g < 12; ++g) f[g] = rotate_bytes(f[g]);
   }
