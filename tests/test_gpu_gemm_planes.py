@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from fp64_gemm_emulation_amd.workloads import WORKLOADS, generate
-from tests.gpu_helpers import assert_equal, compare_sampled, log, sample_indices, to_device
+from tests.gpu_helpers import assert_chat_close, assert_equal, compare_sampled, log, sample_indices, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -210,5 +210,64 @@ def test_k_blocked_production_gemm_every_plane(oz):
     cols = np.array(sorted(set(sample_indices(r, 5, 8).tolist()) | {255, 256, 1279, 1280}))
     compare_sampled(out, oracle.ozaki2_sample(A, B, s, "fast", rows, cols), A, B, s, "fast", rows, cols)
     log("[planes] K-blocked: ok")
+    del out
+    torch.cuda.empty_cache()
+
+
+# Row values of A and column values of B for the INT32-extreme case below: each row of A
+# (column of B) is one constant, so every A'_t (B'_t) entry of a line is one residue and
+# P_t[i, j] = q rho(A'_i) rho(B'_j) exactly.  Chosen (by a search over the oracle's residues
+# of such lines) so that most planes reach |P_t| >= 2^30 and the largest 2^30.97 at
+# q = 131071, the longest inner dimension one launch covers.
+_EXTREME_X = [0.8122686777911212, 0.3467247145518215, 0.09158796504591349, -0.4837182962908233,
+              -0.8651221338159478, 0.4372684343765658, -0.9013546892409319, 0.6037519305692991]
+_EXTREME_Y = [-0.15756668806272445, -0.7597194561131462, -0.022761176011345974, 0.47856384225672954,
+              0.49893093563626234, -0.12307763329453159, -0.22521746631645212, -0.20208214895857712]
+
+
+@pytest.mark.parametrize("q", [(1 << 17) - 1, (1 << 17) + 1000])
+def test_production_gemm_at_int32_extremes(oz, q):
+    """The production GEMM (p = r = 2048, s = 20: 1280 tiles of 256 x 256) with products
+    |P_t| up to 2^30.97, every modulus: A[i, :] = x[i mod 8], B[:, j] = y[j mod 8], so every
+    output of the GPU equals one of the oracle's 8 x 8 outputs of the 8 x q x 8 product with
+    the same lines, and every element of every R_t plane, d, b and C is compared with it.
+    q = 2^17 - 1 is one launch; q = 2^17 + 1000 runs two K-blocks, the second through the
+    accumulate epilogue."""
+    import torch
+    p = r = 2048
+    s = 20
+    assert big_tiles(p, r, s) >= 512
+    xs = np.array(_EXTREME_X)
+    ys = np.array(_EXTREME_Y)
+    log(f"[extremes] oracle on the 8 x {q} x 8 product")
+    ref = oracle.ozaki2(np.repeat(xs[:, None], q, axis=1), np.repeat(ys[None, :], q, axis=0), s, "fast")
+    if q < (1 << 17):
+        pmax = max(int(np.abs(pt).max()) for pt in ref["P"])
+        assert pmax >= 2 ** 30.9, pmax
+    dev = torch.device("cuda")
+    rows = torch.arange(p, device=dev) % 8
+    cols = torch.arange(r, device=dev) % 8
+    A = torch.tensor(xs, device=dev)[rows][:, None].expand(p, q)
+    B = torch.tensor(ys, device=dev)[cols][None, :].expand(q, r)
+    Ad = oz.colmajor(A)
+    Bd = oz.colmajor(B)
+    del A, B
+    log(f"[extremes] p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "R"))
+    torch.cuda.synchronize()
+    del Ad, Bd
+    assert torch.equal(out["d"], torch.tensor(ref["d"].astype(np.int32), device=dev)[rows]), "d"
+    assert torch.equal(out["b"], torch.tensor(ref["b"].astype(np.int32), device=dev)[cols]), "b"
+    for t, m in enumerate(ref["moduli"]):
+        small = torch.tensor(np.asarray(ref["R"][t], dtype=np.uint8), device=dev)   # [i mod 8, j mod 8]
+        want = small.t()[cols][:, rows]                                                # [j, i]
+        got = out["R"][t]
+        if not torch.equal(got, want):
+            jj, ii = (got != want).nonzero()[0].tolist()
+            raise AssertionError(f"R[{t}] (m = {m}) at ({ii}, {jj}): {int(got[jj, ii])} != {int(want[jj, ii])}")
+    c_ref = np.asarray(ref["C"], dtype=np.float64)[np.arange(p)[:, None] % 8, np.arange(r)[None, :] % 8]
+    tol = 4.0 * 2.0 ** -53 * q * np.abs(xs[np.arange(p) % 8][:, None] * ys[np.arange(r) % 8][None, :])
+    assert_chat_close(out["C"].cpu().numpy(), c_ref, tol, "C")
+    log("[extremes] ok: every element of every plane")
     del out
     torch.cuda.empty_cache()
