@@ -225,22 +225,24 @@ _EXTREME_Y = [-0.15756668806272445, -0.7597194561131462, -0.022761176011345974, 
               0.49893093563626234, -0.12307763329453159, -0.22521746631645212, -0.20208214895857712]
 
 
-@pytest.mark.parametrize("q", [(1 << 17) - 1, (1 << 17) + 1000])
-def test_production_gemm_at_int32_extremes(oz, q):
+@pytest.mark.parametrize("mode,q", [("fast", (1 << 17) - 1), ("fast", (1 << 17) + 1000), ("accu", (1 << 17) - 1)])
+def test_production_gemm_at_int32_extremes(oz, mode, q):
     """The production GEMM (p = r = 2048, s = 20: 1280 tiles of 256 x 256) with products
     |P_t| up to 2^30.97, every modulus: A[i, :] = x[i mod 8], B[:, j] = y[j mod 8], so every
     output of the GPU equals one of the oracle's 8 x 8 outputs of the 8 x q x 8 product with
     the same lines, and every element of every R_t plane, d, b and C is compared with it.
     q = 2^17 - 1 is one launch; q = 2^17 + 1000 runs two K-blocks, the second through the
-    accumulate epilogue."""
+    accumulate epilogue.  In accu mode the bound product's row and column maxima over all
+    2048 columns and rows equal those over the 8 distinct ones, so the 8 x q x 8 oracle
+    gives the same exponents as the whole product."""
     import torch
     p = r = 2048
     s = 20
     assert big_tiles(p, r, s) >= 512
     xs = np.array(_EXTREME_X)
     ys = np.array(_EXTREME_Y)
-    log(f"[extremes] oracle on the 8 x {q} x 8 product")
-    ref = oracle.ozaki2(np.repeat(xs[:, None], q, axis=1), np.repeat(ys[None, :], q, axis=0), s, "fast")
+    log(f"[extremes] {mode}: oracle on the 8 x {q} x 8 product")
+    ref = oracle.ozaki2(np.repeat(xs[:, None], q, axis=1), np.repeat(ys[None, :], q, axis=0), s, mode)
     if q < (1 << 17):
         pmax = max(int(np.abs(pt).max()) for pt in ref["P"])
         assert pmax >= 2 ** 30.9, pmax
@@ -252,8 +254,8 @@ def test_production_gemm_at_int32_extremes(oz, q):
     Ad = oz.colmajor(A)
     Bd = oz.colmajor(B)
     del A, B
-    log(f"[extremes] p,q,r={p},{q},{r} s={s}")
-    out = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "R"))
+    log(f"[extremes] {mode}: p,q,r={p},{q},{r} s={s}")
+    out = oz.dgemm_debug(Ad, Bd, s, mode, want=("d", "b", "R"))
     torch.cuda.synchronize()
     del Ad, Bd
     assert torch.equal(out["d"], torch.tensor(ref["d"].astype(np.int32), device=dev)[rows]), "d"
