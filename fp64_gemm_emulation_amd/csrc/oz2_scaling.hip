@@ -33,6 +33,7 @@ constexpr int kStatsRowGroups = 1;
 constexpr int kStatsColGroups = 8;
 constexpr int kStatsCols = kChunk / kStatsColGroups;
 constexpr int kStatsThreads = kWave * kStatsRowGroups * kStatsColGroups;
+constexpr long kComputeUnits = 256;  // MI355X: 8 XCDs of 32
 // Workgroup (bx, c) of the row statistics: rows 64 bx.. of block c.
 template <bool MAXONLY, bool NT>
 __device__ __forceinline__ void stats_rows_block(const double* __restrict__ A, long lda, int p, int q, int nch,
@@ -214,21 +215,36 @@ __global__ __launch_bounds__(256) void stats_cols_kernel(const double* __restric
 }
 
 // Fast-mode statistics of both operands in one launch, for column-major A and B (the
-// untransposed product) that fit the memory-side cache: the first nb_blocks workgroups
-// take the columns of B, 8 waves of (column, CB blocks) items each, the rest the rows of A
-// (grid gxa x nch of stats_rows_block).  On small products the two grids then run side by
-// side instead of one after the other (n = 1024: 12.8 against 15.9 us); on large ones the
-// merged kernel's register count (100, four waves per SIMD against six) made it slower
-// (n = 8192: 0.212 against 0.178 ms), so they keep two launches.
+// untransposed product) that fit the memory-side cache: nb_blocks workgroups take the
+// columns of B, 8 waves of (column, CB blocks) items each, and gxa x nch workgroups the rows
+// of A (one stats_rows_block each).  On small products the two grids then run side by side
+// instead of one after the other (n = 1024: 12.8 against 15.9 us); on large ones the merged
+// kernel, then at 100 registers (four waves per SIMD against six), was slower (n = 8192:
+// 0.212 against 0.178 ms), so they keep two launches.  A row workgroup reads 4x the bytes of
+// a column one; when there are at least as many as compute units they go first, so that
+// they do not form the launch's tail, and the kernel is held to 80 registers so that three
+// workgroups share a CU.  Only the two together paid: n = 2048, 23.0 us against 23.9 (rows
+// first at 100 registers) and 24.2 (columns first, at either count).  With fewer row
+// workgroups columns go first (n = 1024: 12.5 against 12.9 us).
 template <int CB>
-__global__ __launch_bounds__(kStatsThreads) void stats_ab_kernel(const double* __restrict__ A, long lda, int p,
+__global__ __launch_bounds__(kStatsThreads) __attribute__((amdgpu_waves_per_eu(6))) void stats_ab_kernel(const double* __restrict__ A, long lda, int p,
                                                                  const double* __restrict__ B, long ldb, int r,
                                                                  int q, int nch, int gxa, int nb_blocks,
+                                                                 int a_first,
                                                                  int* __restrict__ pe_a, double* __restrict__ ps_a,
                                                                  int* __restrict__ pe_b, double* __restrict__ ps_b) {
   static_assert(kStatsThreads == 8 * kWave, "8 waves per workgroup");
-  const int k = blockIdx.x;
-  if (k < nb_blocks) {
+  const int na_blocks = gxa * nch;
+  int k = blockIdx.x;
+  bool col;  // a workgroup of B's columns; k becomes its index within its operand's grid
+  if (a_first) {
+    col = k >= na_blocks;
+    if (col) k -= na_blocks;
+  } else {
+    col = k < nb_blocks;
+    if (!col) k -= nb_blocks;
+  }
+  if (col) {
     const int groups = (nch + CB - 1) / CB;
     const long item = static_cast<long>(k) * 8 + (threadIdx.x >> 6);
     const int j = static_cast<int>(item / groups);
@@ -236,8 +252,7 @@ __global__ __launch_bounds__(kStatsThreads) void stats_ab_kernel(const double* _
     stats_cols_wave<false, CB, false>(B, ldb, q, r, nch, pe_b, ps_b, nullptr, 0, j,
                                       static_cast<int>(item % groups) * CB);
   } else {
-    const int ka = k - nb_blocks;
-    stats_rows_block<false, false>(A, lda, p, q, nch, pe_a, ps_a, nullptr, 0, ka % gxa, ka / gxa);
+    stats_rows_block<false, false>(A, lda, p, q, nch, pe_a, ps_a, nullptr, 0, k % gxa, k / gxa);
   }
 }
 
@@ -396,10 +411,11 @@ static void stats_lines(const Operand& o, int nlines, int nlines_pad, int q, int
 template <int CB>
 static void launch_stats_ab(const Operand& a, const Operand& b, const Work& w, long nb_blocks, long gxa,
                             hipStream_t st) {
-  const long blocks = nb_blocks + gxa * w.nch;
-  hipLaunchKernelGGL((stats_ab_kernel<CB>), dim3(static_cast<unsigned>(blocks)), dim3(kStatsThreads), 0, st,
-                     a.ptr, a.ld, w.p, b.ptr, b.ld, w.r, w.q, w.nch, static_cast<int>(gxa),
-                     static_cast<int>(nb_blocks), w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b);
+  const long na_blocks = gxa * w.nch;
+  const int a_first = na_blocks >= kComputeUnits ? 1 : 0;
+  hipLaunchKernelGGL((stats_ab_kernel<CB>), dim3(static_cast<unsigned>(nb_blocks + na_blocks)), dim3(kStatsThreads),
+                     0, st, a.ptr, a.ld, w.p, b.ptr, b.ld, w.r, w.q, w.nch, static_cast<int>(gxa),
+                     static_cast<int>(nb_blocks), a_first, w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b);
 }
 
 template <bool MAXONLY>
