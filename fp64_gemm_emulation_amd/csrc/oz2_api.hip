@@ -308,6 +308,7 @@ int run(const Call& c, void* stream, const oz2_dump_t* dump, bool use_scratch = 
   // rows of op(A) are contiguous when A is transposed; columns of op(B) unless B is
   const oz2::Operand opa{c.A, c.lda, c.transa == OZ2_OP_T};
   const oz2::Operand opb{c.B, c.ldb, c.transb == OZ2_OP_N};
+  w.exp_in_residues = oz2::exponents_in_residues(opa, opb, w, dp);
   // --- scaling ---
   if (!accu) {
     OZ2_TRY(oz2::launch_fast_scaling(opa, opb, w, st));
@@ -323,11 +324,12 @@ int run(const Call& c, void* stream, const oz2_dump_t* dump, bool use_scratch = 
     if (dz.gamma != nullptr)
       OZ2_TRY(hipMemcpyAsync(dz.gamma, w.gamma, sizeof(int) * r, hipMemcpyDeviceToDevice, st));
   }
-  if (dz.d != nullptr) OZ2_TRY(hipMemcpyAsync(dz.d, w.d, sizeof(int) * p, hipMemcpyDeviceToDevice, st));
-  if (dz.b != nullptr) OZ2_TRY(hipMemcpyAsync(dz.b, w.b, sizeof(int) * r, hipMemcpyDeviceToDevice, st));
   OZ2_TRY(rec.mark(1));
   // --- residues ---
   OZ2_TRY(oz2::launch_residues(opa, opb, w, dp, st));
+  // (d and b are final here: for small fast-mode products the residue launch computes them)
+  if (dz.d != nullptr) OZ2_TRY(hipMemcpyAsync(dz.d, w.d, sizeof(int) * p, hipMemcpyDeviceToDevice, st));
+  if (dz.b != nullptr) OZ2_TRY(hipMemcpyAsync(dz.b, w.b, sizeof(int) * r, hipMemcpyDeviceToDevice, st));
   if (dz.At != nullptr) OZ2_TRY(oz2::launch_unpack_operands(w.at, w.at_plane, s, p, q, w.q_pad, dz.At, st));
   if (dz.Bt != nullptr) OZ2_TRY(oz2::launch_unpack_operands(w.bt, w.bt_plane, s, r, q, w.q_pad, dz.Bt, st));
   OZ2_TRY(rec.mark(2));

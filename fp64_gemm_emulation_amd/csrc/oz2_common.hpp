@@ -77,6 +77,60 @@ __device__ __forceinline__ int clog2_u64(uint64_t v) {
   return v <= 1 ? 0 : 64 - __clzll(static_cast<long long>(v - 1));
 }
 
+// Reductions over G consecutive lanes (a power of two, at most 64); every lane of the group
+// receives the result.
+template <int G>
+__device__ __forceinline__ int group_max(int v) {
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ uint64_t group_sum_u64(uint64_t v) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) {
+    const uint32_t lo2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off, kWave));
+    const uint32_t hi2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off, kWave));
+    const uint32_t sum = lo + lo2;
+    hi = hi + hi2 + (sum < lo ? 1u : 0u);
+    lo = sum;
+  }
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Fast-mode exponent of one line ("Profiling Ozaki II: The Cost Behind Fast INT8 GEMMs",
+// Part I section 2) from its statistics partials: block c has max-abs exponent e_c
+// (kNoExp when all zero) and the exact integer sum of squares S_c at that exponent.  With
+// e = max_c e_c (not kNoExp) and S = sum_c ceil(S_c / 4^(e - e_c)) the exponent is
+// floor((tau - ceil(log2 S)) / 2) + kFBits - e; an all-zero line gets 0.  S is exact in
+// uint64 (at most q 2^40 < 2^59), so the order of the sums does not matter.
+// One block's term ceil(S_c / 4^(e - e_c)), 0 for an all-zero block, without branches
+// (ceil_shift's for a shift clamped to 60: 0 < S_c < 2^53 then leaves a value in (0, 1)
+// whose ceiling is 1, the value of every larger shift).
+__device__ __forceinline__ uint64_t partial_at_line_scale(int e, int ec, double sc) {
+  const double v = ec == kNoExp ? 0.0 : sc;
+  return static_cast<uint64_t>(ceil(ldexp(v, -2 * min(e - ec, 30))));
+}
+
+__device__ __forceinline__ int fast_exponent(int e, uint64_t S, int tau) {
+  return ((tau - clog2_u64(S)) >> 1) + kFBits - e;
+}
+
+// The same with G consecutive lanes sharing the line, lane g of the group reading blocks
+// g, g + G, ... < nch of pe / ps; every lane of the group returns the exponent.
+template <int G>
+__device__ __forceinline__ int fast_line_exponent(const int* pe, const double* ps, int nch, int g, int tau) {
+  int e = kNoExp;
+  for (int c = g; c < nch; c += G) e = max(e, pe[c]);
+  e = group_max<G>(e);
+  if (e == kNoExp) return 0;  // uniform over the group
+  uint64_t S = 0;
+  for (int c = g; c < nch; c += G) S += partial_at_line_scale(e, pe[c], ps[c]);
+  return fast_exponent(e, group_sum_u64<G>(S), tau);
+}
+
 // Operand planes (A_t, B_t and the accu quantized operands) are stored in the order the
 // GEMM consumes them, tile-contiguous:
 //   [256-row block][64-byte stage of the inner dimension][256 rows x 64 bytes],

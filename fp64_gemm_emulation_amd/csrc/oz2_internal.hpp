@@ -16,6 +16,8 @@ struct Work {
   int nch;                  // number of kChunk-long blocks along q
   int tau;
   bool stream_inputs;       // FP64 operand reads with the non-temporal hint (large operands)
+  bool exp_in_residues;     // fast mode: the residue launch computes d and b from the statistics
+                            // partials (no exponent launch); see exponents_in_residues
   unsigned* flags;          // 1 word
   int* d;                   // [p]   row exponents of A
   int* b;                   // [r]   column exponents of B
@@ -60,6 +62,9 @@ hipError_t launch_accu_bound_inputs(const Operand& a, const Operand& b, const Wo
 hipError_t launch_accu_exponents(const Work& w, hipStream_t st);
 
 // residue stage
+// Whether the fast-mode exponents can be computed inside the residue launch for these
+// operands (small untransposed products with short inner dimensions, no A' / B' dumps).
+bool exponents_in_residues(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump);
 hipError_t launch_residues(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump,
                            hipStream_t st);
 

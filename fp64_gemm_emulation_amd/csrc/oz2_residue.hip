@@ -145,25 +145,112 @@ struct ResidueOperand {
   long plane;
 };
 
+// Statistics partials of one operand's lines, for the residue launch that computes the
+// fast-mode exponents itself: the partials of line n at pe[n nch ..] and ps[n nch ..]
+// (fast_line_exponent); the exponents are stored to out.  That launch is used for at most
+// kExpInResiduesBlocks blocks per line (exponents_in_residues).
+constexpr int kExpInResiduesBlocks = 16;
+
+struct LineStats {
+  const int* pe;
+  const double* ps;
+  int nch;
+  int tau;
+  int* out;
+};
+
+// One lane's share of a line's partials, when G lanes share the line: blocks g + G t.
+template <int G>
+struct LinePartials {
+  static constexpr int K = kExpInResiduesBlocks / G;
+  int e[K];
+  double s[K];
+};
+
+// The loads are unconditional, from clamped in-range addresses (line 0 and block nch - 1
+// exist on this path), and the unused values are replaced afterwards: with no branch
+// around them the wait for these first loads does not also wait for the element loads
+// issued after them.
+template <int G>
+__device__ __forceinline__ LinePartials<G> load_partials(const LineStats& ls, int n, bool ok, int g) {
+  LinePartials<G> lp;
+  const long off = static_cast<long>(ok ? n : 0) * ls.nch;
+#pragma unroll
+  for (int t = 0; t < LinePartials<G>::K; ++t) {
+    const int c = g + t * G;
+    const long at = off + min(c, ls.nch - 1);
+    const int ev = ls.pe[at];
+    const double sv = ls.ps[at];
+    const bool in = ok && c < ls.nch;
+    lp.e[t] = in ? ev : kNoExp;
+    lp.s[t] = in ? sv : 0.0;
+  }
+  return lp;
+}
+
+// Exponent of line n from the partials the group's lanes hold (fast_line_exponent's
+// arithmetic); the workgroups of the first inner-dimension block (by == 0) store it for
+// the later stages.
+template <int G>
+__device__ __forceinline__ int line_exponent(const LinePartials<G>& lp, const LineStats& ls, int n, bool ok, int by,
+                                             int g) {
+  int e = kNoExp;
+#pragma unroll
+  for (int t = 0; t < LinePartials<G>::K; ++t) e = max(e, lp.e[t]);
+  e = group_max<G>(e);
+  // (no branch on an all-zero line, whose terms are all 0: a branch would move the
+  // loads of the sums after the element loads)
+  uint64_t S = 0;
+#pragma unroll
+  for (int t = 0; t < LinePartials<G>::K; ++t) S += partial_at_line_scale(e, lp.e[t], lp.s[t]);
+  S = group_sum_u64<G>(S);
+  const int sc = e == kNoExp ? 0 : fast_exponent(e, S, ls.tau);
+  if (ok && by == 0 && g == 0) ls.out[n] = sc;
+  return sc;
+}
+
 // Lines that are rows of a column-major matrix (rows of A, or columns of op(B) = B^T);
 // thread mapping owner_rows_of_a for workgroup (bx, by) (the thread's 16 elements of line i
 // are l = 256 blk + L + 16 k).  The validation dump of the scaled operand receives element
 // (line, l) at ap_dump[line dls + l dks].  A non-finite input (read as 0) sets the flag word.
-// NT: non-temporal reads of the operand (Work::stream_inputs).
-template <int S, int ND, bool DUMP, bool NT>
+// NT: non-temporal reads of the operand (Work::stream_inputs).  FUSE: the line exponents
+// come from the statistics partials (line_exponent); the partials are loaded first and
+// the elements next, so that the exponent's arithmetic runs while the elements arrive.
+template <int S, int ND, bool DUMP, bool NT, bool FUSE = false>
 __device__ __forceinline__ void residues_rows_block(const ResidueOperand& o, int q, int q_pad, int bx, int by,
-                                                    unsigned* flags, double* ap_dump, long dls, long dks) {
+                                                    unsigned* flags, double* ap_dump, long dls, long dks,
+                                                    const LineStats& ls = LineStats{}) {
   const ChunkOwner own = owner_rows_of_a(bx, by);
   const int i = own.row;
   const bool row_ok = i < o.nlines;
-  const int scale = row_ok ? o.scale[i] : 0;
+  const int lg = threadIdx.x & 3;  // the 4 lanes of a row are consecutive (owner_rows_of_a)
+  double xs[16];
+  int scale;
+  if constexpr (FUSE) {
+    // (unconditional loads from clamped addresses, as in load_partials; q >= 1 here)
+    const LinePartials<4> lp = load_partials<4>(ls, i, row_ok, lg);
+    const double* line = o.ptr + (row_ok ? i : 0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int col = own.blk * kKPad + own.slot + 16 * k;
+      const double v = load_f64<NT>(line + static_cast<long>(min(col, q - 1)) * o.ld);
+      xs[k] = row_ok && col < q ? v : 0.0;
+    }
+    scale = line_exponent<4>(lp, ls, i, row_ok, by, lg);
+  } else {
+    scale = row_ok ? o.scale[i] : 0;
+  }
   ScaledDigits g[16];
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int col = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = row_ok && col < q;
-    const double x = ok ? load_f64<NT>(o.ptr + i + static_cast<long>(col) * o.ld) : 0.0;
+    double x;
+    if constexpr (FUSE)
+      x = xs[k];
+    else
+      x = ok ? load_f64<NT>(o.ptr + i + static_cast<long>(col) * o.ld) : 0.0;
     bad |= !__builtin_isfinite(x);
     double apv;
     g[k] = scaled_digits(x, scale, DUMP ? &apv : nullptr);
@@ -176,22 +263,42 @@ __device__ __forceinline__ void residues_rows_block(const ResidueOperand& o, int
 }
 
 // Contiguous lines (columns of B, or rows of op(A) = A^T); thread mapping owner_cols_of_b
-// for workgroup (bx, by).  Dump, flag and NT as in residues_rows_block.
-template <int S, int ND, bool DUMP, bool NT>
+// for workgroup (bx, by).  Dump, flag, NT and FUSE as in residues_rows_block.
+template <int S, int ND, bool DUMP, bool NT, bool FUSE = false>
 __device__ __forceinline__ void residues_cols_block(const ResidueOperand& o, int q, int q_pad, int bx, int by,
-                                                    unsigned* flags, double* bp_dump, long dls, long dks) {
+                                                    unsigned* flags, double* bp_dump, long dls, long dks,
+                                                    const LineStats& ls = LineStats{}) {
   const ChunkOwner own = owner_cols_of_b(bx, by);
   const int j = own.row;
   const bool col_ok = j < o.nlines;
-  const int scale = col_ok ? o.scale[j] : 0;
   const double* col = o.ptr + static_cast<long>(col_ok ? j : 0) * o.ld;
+  const int lg = threadIdx.x & 15;  // the 16 lanes of a column are consecutive (owner_cols_of_b)
+  double xs[16];
+  int scale;
+  if constexpr (FUSE) {
+    // (unconditional loads from clamped addresses, as in load_partials; q >= 1 here)
+    const LinePartials<16> lp = load_partials<16>(ls, j, col_ok, lg);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = own.blk * kKPad + own.slot + 16 * k;
+      const double v = load_f64<NT>(col + min(row, q - 1));
+      xs[k] = col_ok && row < q ? v : 0.0;
+    }
+    scale = line_exponent<16>(lp, ls, j, col_ok, by, lg);
+  } else {
+    scale = col_ok ? o.scale[j] : 0;
+  }
   ScaledDigits g[16];
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int row = own.blk * kKPad + own.slot + 16 * k;
     const bool ok = col_ok && row < q;
-    const double x = ok ? load_f64<NT>(col + row) : 0.0;
+    double x;
+    if constexpr (FUSE)
+      x = xs[k];
+    else
+      x = ok ? load_f64<NT>(col + row) : 0.0;
     bad |= !__builtin_isfinite(x);
     double bpv;
     g[k] = scaled_digits(x, scale, DUMP ? &bpv : nullptr);
@@ -216,17 +323,18 @@ __global__ __launch_bounds__(256) void residues_kernel(ResidueOperand o, int q, 
 // Both operands in one launch, for column-major A and B (the untransposed product): the
 // first nb_blocks workgroups take the columns of B (grid gxb wide), the rest the rows of A
 // (grid gxa wide).  One launch instead of two saves a dependent kernel start and the ramp
-// and tail of a second grid, which matter at small sizes.
-template <int S, int ND, bool NT>
+// and tail of a second grid, which matter at small sizes.  FUSE: the fast-mode exponents
+// are computed here from the statistics partials la, lb (exponents_in_residues).
+template <int S, int ND, bool NT, bool FUSE>
 __global__ __launch_bounds__(256) void residues_ab_kernel(ResidueOperand a, ResidueOperand b, int q, int q_pad,
                                                           int gxa, int gxb, int nb_blocks,
-                                                          unsigned* __restrict__ flags) {
+                                                          unsigned* __restrict__ flags, LineStats la, LineStats lb) {
   const int k = blockIdx.x;
   if (k < nb_blocks)
-    residues_cols_block<S, ND, false, NT>(b, q, q_pad, k % gxb, k / gxb, flags, nullptr, 0, 0);
+    residues_cols_block<S, ND, false, NT, FUSE>(b, q, q_pad, k % gxb, k / gxb, flags, nullptr, 0, 0, lb);
   else
-    residues_rows_block<S, ND, false, NT>(a, q, q_pad, (k - nb_blocks) % gxa, (k - nb_blocks) / gxa, flags, nullptr,
-                                          0, 0);
+    residues_rows_block<S, ND, false, NT, FUSE>(a, q, q_pad, (k - nb_blocks) % gxa, (k - nb_blocks) / gxa, flags,
+                                                nullptr, 0, 0, la);
 }
 
 // Grid of one operand's residue launch: (lines / 16, q_pad / 256) for contiguous lines, else
@@ -262,8 +370,19 @@ static void launch_residues_nt(const Operand& a, const Operand& b, const Work& w
   if (!a.contig && b.contig && nb + na < (1L << 24)) {
     const ResidueOperand ra{a.ptr, a.ld, w.p, w.d, w.at, w.at_plane};
     const ResidueOperand rb{b.ptr, b.ld, w.r, w.b, w.bt, w.bt_plane};
-    hipLaunchKernelGGL((residues_ab_kernel<S, NL, NT>), dim3(static_cast<unsigned>(nb + na)), dim3(256), 0, st, ra,
-                       rb, w.q, w.q_pad, static_cast<int>(ga.x), static_cast<int>(gb.x), static_cast<int>(nb), w.flags);
+    if constexpr (!ACCU && !NT) {
+      if (w.exp_in_residues) {
+        const LineStats la{w.part_e_a, w.part_s_a, w.nch, w.tau, w.d};
+        const LineStats lb{w.part_e_b, w.part_s_b, w.nch, w.tau, w.b};
+        hipLaunchKernelGGL((residues_ab_kernel<S, NL, false, true>), dim3(static_cast<unsigned>(nb + na)), dim3(256),
+                           0, st, ra, rb, w.q, w.q_pad, static_cast<int>(ga.x), static_cast<int>(gb.x),
+                           static_cast<int>(nb), w.flags, la, lb);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((residues_ab_kernel<S, NL, NT, false>), dim3(static_cast<unsigned>(nb + na)), dim3(256), 0, st,
+                       ra, rb, w.q, w.q_pad, static_cast<int>(ga.x), static_cast<int>(gb.x), static_cast<int>(nb),
+                       w.flags, LineStats{}, LineStats{});
     return;
   }
   residues_lines<S, NL, false, NT>(b, w.r, w.r_pad, w.q, w.q_pad, w.b, w.bt, w.bt_plane, w.flags, nullptr, 0L, 0L, st);
@@ -313,6 +432,21 @@ static bool dispatch_residues(int s, const Operand& a, const Operand& b, const W
     }
     return dispatch_residues<S + 1>(s, a, b, w, dump, st);
   }
+}
+
+// Fast mode moves the exponents into the residue launch when that launch takes both
+// operands (untransposed, below 2^24 workgroups) without the non-temporal hint (so the
+// statistics of both ran in one launch, which clears the flag word), no A' / B' dump is
+// requested (the dumping kernels read d and b), and the inner dimension has at most
+// kExpInResiduesBlocks 256-blocks: every residue workgroup that covers a line recomputes
+// its exponent (q / 64 of them for a row of A, q / 256 for a column of B), so those reads
+// of partials grow with q^2 per line.
+
+bool exponents_in_residues(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump) {
+  if (w.accu || w.stream_inputs || a.contig || !b.contig || dump.ap != nullptr || dump.bp != nullptr) return false;
+  if (w.nch <= 0 || w.nch > kExpInResiduesBlocks || w.p <= 0 || w.r <= 0) return false;
+  const dim3 ga = residue_grid(false, w.p_pad, w.q_pad), gb = residue_grid(true, w.r_pad, w.q_pad);
+  return static_cast<long>(ga.x) * ga.y + static_cast<long>(gb.x) * gb.y < (1L << 24);
 }
 
 hipError_t launch_residues(const Operand& a, const Operand& b, const Work& w, const DumpPtrs& dump,

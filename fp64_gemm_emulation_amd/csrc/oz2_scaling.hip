@@ -232,8 +232,12 @@ __global__ __launch_bounds__(kStatsThreads) __attribute__((amdgpu_waves_per_eu(6
                                                                  int q, int nch, int gxa, int nb_blocks,
                                                                  int a_first,
                                                                  int* __restrict__ pe_a, double* __restrict__ ps_a,
-                                                                 int* __restrict__ pe_b, double* __restrict__ ps_b) {
+                                                                 int* __restrict__ pe_b, double* __restrict__ ps_b,
+                                                                 unsigned* __restrict__ flags) {
   static_assert(kStatsThreads == 8 * kWave, "8 waves per workgroup");
+  // the call's non-finite flag starts here when the residue kernel computes the exponents
+  // itself (no exponent launch, which otherwise clears it again)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   const int na_blocks = gxa * nch;
   int k = blockIdx.x;
   bool col;  // a workgroup of B's columns; k becomes its index within its operand's grid
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(kStatsThreads) __attribute__((amdgpu_waves_per_eu(6
 }
 
 // One wave per line (rows of A first, then columns of B): combine the block partials, the
-// lanes taking blocks lane, lane + 64, ...  S is exact in uint64 (at most q 2^40 < 2^59).
+// lanes taking blocks lane, lane + 64, ...
 __global__ __launch_bounds__(256) void fast_exponents_kernel(int na, int nb, int nch, const int* __restrict__ pe_a,
                                                              const double* __restrict__ ps_a,
                                                              const int* __restrict__ pe_b,
@@ -266,36 +270,14 @@ __global__ __launch_bounds__(256) void fast_exponents_kernel(int na, int nb, int
                                                              unsigned* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
-  // the call's non-finite flag starts here: the residue stage, which runs after this
-  // kernel, sets it (no earlier kernel of the call touches it)
+  // the call's non-finite flag starts here (the merged statistics launch clears it too):
+  // the residue stage, which runs after this kernel, sets it
   if (blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   if (idx >= na + nb) return;  // whole wave
   const bool is_a = idx < na;
   const int line = is_a ? idx : idx - na;
-  const int* pe = (is_a ? pe_a : pe_b) + static_cast<long>(line) * nch;
-  const double* ps = (is_a ? ps_a : ps_b) + static_cast<long>(line) * nch;
-  int e = kNoExp;
-  for (int c = lane; c < nch; c += kWave) e = max(e, pe[c]);
-  e = wave_max(e);
-  int out = 0;
-  if (e != kNoExp) {
-    uint64_t S = 0;
-    for (int c = lane; c < nch; c += kWave) {
-      const int ec = pe[c];
-      if (ec != kNoExp) S += ceil_shift(ps[c], 2 * (e - ec));
-    }
-    uint32_t lo = static_cast<uint32_t>(S), hi = static_cast<uint32_t>(S >> 32);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t lo2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off, kWave));
-      const uint32_t hi2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off, kWave));
-      const uint32_t sum = lo + lo2;
-      hi = hi + hi2 + (sum < lo ? 1u : 0u);
-      lo = sum;
-    }
-    S = (static_cast<uint64_t>(hi) << 32) | lo;
-    out = ((tau - clog2_u64(S)) >> 1) + kFBits - e;
-  }
+  const long off = static_cast<long>(line) * nch;
+  const int out = fast_line_exponent<kWave>((is_a ? pe_a : pe_b) + off, (is_a ? ps_a : ps_b) + off, nch, lane, tau);
   if (lane == 0) {
     if (is_a)
       d[line] = out;
@@ -415,7 +397,8 @@ static void launch_stats_ab(const Operand& a, const Operand& b, const Work& w, l
   const int a_first = na_blocks >= kComputeUnits ? 1 : 0;
   hipLaunchKernelGGL((stats_ab_kernel<CB>), dim3(static_cast<unsigned>(nb_blocks + na_blocks)), dim3(kStatsThreads),
                      0, st, a.ptr, a.ld, w.p, b.ptr, b.ld, w.r, w.q, w.nch, static_cast<int>(gxa),
-                     static_cast<int>(nb_blocks), a_first, w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b);
+                     static_cast<int>(nb_blocks), a_first, w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b,
+                     w.flags);
 }
 
 template <bool MAXONLY>
@@ -452,7 +435,7 @@ static void requant_lines(int8_t* plane, int nlines, int nch, int q_pad, const i
 
 hipError_t launch_fast_scaling(const Operand& a, const Operand& b, const Work& w, hipStream_t st) {
   hipError_t e = launch_stats<false>(a, b, w, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || w.exp_in_residues) return e;
   const int n = w.p + w.r;
   hipLaunchKernelGGL(fast_exponents_kernel, dim3(blocks_for(n, 4)), dim3(256), 0, st, w.p, w.r, w.nch,
                      w.part_e_a, w.part_s_a, w.part_e_b, w.part_s_b, w.d, w.b, w.tau, w.flags);

@@ -1,0 +1,64 @@
+"""Fast-mode scaling exponents computed inside the residue launch ("Profiling Ozaki II: The
+Cost Behind Fast INT8 GEMMs", Part I section 2).
+
+For small untransposed fast-mode products with inner dimensions up to 16 blocks of 256,
+the residue launch combines each line's statistics partials itself instead of reading d
+and b from a separate exponent launch.  A call that requests the A' dump takes the other
+path (separate exponent launch, dumping residue kernels), so the two paths can be run on
+the same inputs: d, b, every R_t plane, X and C must be identical, and d, b must equal
+the oracle's exponents.  The inputs carry the cases the combination has to get right:
+all-zero lines, lines whose leading or trailing blocks are zero, lines far below and
+above 1 in magnitude, and block counts 1, 3, 16 (the largest on this path) and 17 (the
+smallest off it).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp64_gemm_emulation_amd.workloads import generate
+from tests.gpu_helpers import assert_equal, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def oz():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    from fp64_gemm_emulation_amd import binding
+    return binding
+
+
+def _operands(p, q, r, seed):
+    A = generate(p, q, 0.5, seed)
+    B = generate(q, r, 0.5, seed + 1)
+    A[min(5, p - 1), :] = 0.0                        # all-zero row
+    B[:, min(3, r - 1)] = 0.0                        # all-zero column
+    if q > 256:
+        A[min(7, p - 1), :256] = 0.0                 # leading block zero
+        B[256:, min(6, r - 1)] = 0.0                 # only the first block nonzero
+    A[min(9, p - 1), :] *= 2.0 ** -600               # far below 1
+    B[:, min(4, r - 1)] *= 2.0 ** 500                # far above 1
+    A[min(11, p - 1), q // 2] = 3.0 ** 40            # one dominant element
+    return A, B
+
+
+@pytest.mark.parametrize("s", [8, 14, 20])
+@pytest.mark.parametrize("shape", [(300, 517, 129), (257, 4096, 255), (64, 4097, 70), (40, 200, 33), (1, 1, 1)])
+def test_exponents_in_residue_launch_match_the_exponent_launch(oz, shape, s):
+    import torch
+    p, q, r = shape
+    A, B = _operands(p, q, r, 700 + q)
+    Ad, Bd = to_device(A), to_device(B)
+    log(f"[exp in residues] p,q,r={p},{q},{r} s={s}")
+    inres = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "R", "X"))
+    separate = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "Ap", "R", "X"))
+    for k in ("d", "b", "R", "X"):
+        assert torch.equal(inres[k], separate[k]), f"{k} differs between the two exponent paths"
+    assert torch.equal(inres["C"].view(torch.int64), separate["C"].view(torch.int64)), "C differs"
+    d_ref, _, _ = oracle.fast_exponents(A, s)
+    b_ref, _, _ = oracle.fast_exponents(np.ascontiguousarray(B.T), s)
+    assert_equal(inres["d"].cpu().numpy(), d_ref.astype(np.int32), "d")
+    assert_equal(inres["b"].cpu().numpy(), b_ref.astype(np.int32), "b")
+    log("[exp in residues] ok")
