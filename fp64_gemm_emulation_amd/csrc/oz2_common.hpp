@@ -26,11 +26,6 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
-__device__ __forceinline__ int wave_max_w(int v, int width) {
-  for (int off = width / 2; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);

@@ -9,7 +9,7 @@ the same inputs: d, b, every R_t plane, X and C must be identical, and d, b must
 the oracle's exponents.  The inputs carry the cases the combination has to get right:
 all-zero lines, lines whose leading or trailing blocks are zero, lines far below and
 above 1 in magnitude, and block counts 1, 3, 16 (the largest on this path) and 17 (the
-smallest off it).
+smallest off it), and the full-size 2048^3 product.
 """
 import numpy as np
 import pytest
@@ -44,9 +44,13 @@ def _operands(p, q, r, seed):
     return A, B
 
 
-@pytest.mark.parametrize("s", [8, 14, 20])
-@pytest.mark.parametrize("shape", [(300, 517, 129), (257, 4096, 255), (64, 4097, 70), (40, 200, 33), (1, 1, 1)])
+@pytest.mark.parametrize("s,shape", [(s, shape) for s in (8, 14, 20)
+                                     for shape in ((300, 517, 129), (257, 4096, 255), (64, 4097, 70), (40, 200, 33),
+                                                   (1, 1, 1))]
+                         + [(14, (2048, 2048, 2048)), (14, (1024, 4096, 1024))])
 def test_exponents_in_residue_launch_match_the_exponent_launch(oz, shape, s):
+    """The last two shapes have at least one row-statistics workgroup per compute unit, so
+    the merged statistics launch also takes its rows-first order."""
     import torch
     p, q, r = shape
     A, B = _operands(p, q, r, 700 + q)
