@@ -197,7 +197,9 @@ int ozaki2_dgemm_debug(int p, int q, int r, const double* A, int lda, const doub
  * the four stages.  ozaki2_timing_end synchronizes on the last recorded event and returns
  * the per-stage sums in milliseconds over the timed calls:
  *   stage_ms[0] scaling   (fast: statistics + exponents; accu: bound inputs, bound GEMM, exponents)
- *   stage_ms[1] residues  (scale, truncate and all s centered int8 residues of A and B)
+ *   stage_ms[1] residues  (scale, truncate and all s centered int8 residues of A and B; for small
+ *                          untransposed fast-mode products, whose exponents this launch computes
+ *                          from the statistics, also the exponents)
  *   stage_ms[2] gemm      (the batched s INT8 GEMMs with the fused mod-m epilogue)
  *   stage_ms[3] crt       (CRT reconstruction and inverse scaling into C)
  * and in *ncalls the number of calls timed.  Timing is then switched off.
