@@ -66,3 +66,28 @@ def test_exponents_in_residue_launch_match_the_exponent_launch(oz, shape, s):
     assert_equal(inres["d"].cpu().numpy(), d_ref.astype(np.int32), "d")
     assert_equal(inres["b"].cpu().numpy(), b_ref.astype(np.int32), "b")
     log("[exp in residues] ok")
+
+
+@pytest.mark.parametrize("s", [8, 14])
+def test_exponents_in_residue_launch_with_padded_leading_dimensions(oz, s):
+    """The same comparison with leading dimensions larger than the matrices (the residue
+    launch's clamped element addresses run over each line's own stride)."""
+    import torch
+    p, q, r = 200, 700, 150
+    A, B = _operands(p, q, r, 901)
+    Abig = torch.full((q, p + 56), float("nan"), dtype=torch.float64, device="cuda").t()   # ld p + 56
+    Abig[:p, :] = to_device(A)
+    Bbig = torch.full((r, q + 100), float("nan"), dtype=torch.float64, device="cuda").t()  # ld q + 100
+    Bbig[:q, :] = to_device(B)
+    Ad, Bd = Abig[:p, :], Bbig[:q, :]
+    log(f"[exp in residues] padded p,q,r={p},{q},{r} s={s}")
+    inres = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "R", "X"))
+    rc, flags = oz.ozaki2_get_flags()
+    assert rc == oz.OZ2_OK and flags == 0  # the NaN padding is never read
+    separate = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "Ap", "R", "X"))
+    for k in ("d", "b", "R", "X"):
+        assert torch.equal(inres[k], separate[k]), f"{k} differs between the two exponent paths"
+    assert torch.equal(inres["C"].view(torch.int64), separate["C"].view(torch.int64)), "C differs"
+    d_ref, _, _ = oracle.fast_exponents(A, s)
+    assert_equal(inres["d"].cpu().numpy(), d_ref.astype(np.int32), "d")
+    log("[exp in residues] ok")
