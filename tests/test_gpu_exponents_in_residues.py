@@ -91,3 +91,28 @@ def test_exponents_in_residue_launch_with_padded_leading_dimensions(oz, s):
     d_ref, _, _ = oracle.fast_exponents(A, s)
     assert_equal(inres["d"].cpu().numpy(), d_ref.astype(np.int32), "d")
     log("[exp in residues] ok")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_exponents_in_residue_launch_random_shapes(oz, case):
+    """Seeded random shapes (p, r up to 700, q up to 6000, so both sides of the 16-block
+    limit) and input spreads, both exponent paths compared as above."""
+    import torch
+    rng = np.random.default_rng(4100 + case)
+    p, q, r = (int(rng.integers(1, 701)), int(rng.integers(1, 6001)), int(rng.integers(1, 701)))
+    s = int(rng.choice([2, 6, 11, 14, 17, 20]))
+    phi = float(rng.choice([0.0, 0.5, 1.0, 2.0]))
+    A = generate(p, q, phi, 5000 + case)
+    B = generate(q, r, phi, 6000 + case)
+    Ad, Bd = to_device(A), to_device(B)
+    log(f"[exp in residues] random case {case}: p,q,r={p},{q},{r} s={s} phi={phi}")
+    inres = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "R", "X"))
+    separate = oz.dgemm_debug(Ad, Bd, s, "fast", want=("d", "b", "Ap", "R", "X"))
+    for k in ("d", "b", "R", "X"):
+        assert torch.equal(inres[k], separate[k]), f"{k} differs between the two exponent paths"
+    assert torch.equal(inres["C"].view(torch.int64), separate["C"].view(torch.int64)), "C differs"
+    d_ref, _, _ = oracle.fast_exponents(A, s)
+    b_ref, _, _ = oracle.fast_exponents(np.ascontiguousarray(B.T), s)
+    assert_equal(inres["d"].cpu().numpy(), d_ref.astype(np.int32), "d")
+    assert_equal(inres["b"].cpu().numpy(), b_ref.astype(np.int32), "b")
+    log("[exp in residues] ok")
